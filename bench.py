@@ -1,0 +1,125 @@
+"""Benchmark of the relative-attention hot path on one MI355X.
+
+One step = one fused relative-attention forward at B=8, H=16, dh=64, L=512,
+M=512 (bf16 in, fp32 accumulate) plus the Tail_M update of that layer's
+memory (B=8, M=512, d=H*dh=1024, bf16).  Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
+
+Prints one JSON line.  value = algorithmic TFLOP/s of the whole step:
+F_alg = 6 * dh * B * H * V with V = L*M + L*(L+1)/2 visible (query, key)
+pairs per head (three contractions over the visible pairs).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_alg(B, H, L, M, dh):
+    vis = L * M + L * (L + 1) // 2
+    return 6.0 * dh * B * H * vis
+
+
+def min_bytes(B, H, L, M, dh, es=2):
+    K = M + L
+    return es * (2 * B * H * L * dh + 2 * B * H * K * dh + H * K * dh)
+
+
+def cpu_baseline(d, B, H, L, M, dh, heads=16):
+    """Time the oracle on a bounded sample: the first `heads` (b, h) units of
+    the workload, split over the host's cores (each head is independent)."""
+    import oracle
+
+    threads = min(os.cpu_count() or 1, 16, heads)
+    t0 = time.perf_counter()
+    oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=threads, bh_range=(0, heads))
+    dt = time.perf_counter() - t0
+    f = flops_alg(B, H, L, M, dh) * heads / (B * H)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {B * H} (b,h) heads of the same workload, fp64 scalar C, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_xl_relative_rel_amd as txl
+    from transformer_xl_relative_rel_amd import synth
+
+    dev = "cuda:0"
+    B, H, L, M, dh = 8, 16, 512, 512, 64
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    q, k, v, r = (t(d[x], torch.bfloat16) for x in ("q", "k", "v", "r"))
+    u, vb = t(d["u"], torch.float32), t(d["vb"], torch.float32)
+    out = torch.empty_like(q)
+    D = H * dh
+    mem = torch.from_numpy(synth.round_bf16(synth.normal((B, M, D), synth.STREAM["mem"]))).to(dev).to(torch.bfloat16)
+    h = torch.from_numpy(synth.round_bf16(synth.normal((B, L, D), synth.STREAM["h"]))).to(dev).to(torch.bfloat16)
+    new_mem = torch.empty_like(mem)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        txl.relattn_fwd(q, k, v, r, u, vb, out=out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        txl.mem_update(mem, h, M, out=new_mem, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    F = flops_alg(B, H, L, M, dh)
+    value = F / (ms_step * 1e-3) / 1e12
+    achieved = F / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "rel-attn fwd TFLOP/s + % bf16 MFMA peak at B=8,H=16,dh=64,L=512,M=512",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "relattn_fwd+mem_update B8 H16 dh64 L512 M512 bf16", "B": B, "H": H, "dh": dh,
+                   "L": L, "M": M, "parallelism": "single-gpu"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "relattn_fwd_kernel<bf16,64,2>", "kernel_ms": round(attn_ms, 5)},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(d, B, H, L, M, dh)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * txl.h -- C ABI of the MI355X (gfx950) Transformer-XL relative-attention
+ * library, libtxl.so.
+ *
+ * Sources (web pages; cited by title and section / class):
+ *   [SRC] "Transformer-XL模型 核心源码阅读笔记" (source-reading notes,
+ *         blog.csdn.net/ACM_hades/article/details/104742528)
+ *   [XL]  "Transformer-XL" (textbook notes, zty624.github.io, DL notebooks,
+ *         ch4_transformer/xl)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains them.  Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL = the null stream) and is
+ *     asynchronous: a call returning TXL_OK has validated its arguments and
+ *     launched; faults inside kernels surface at the caller's next
+ *     synchronisation of that stream.
+ *   - Every argument check runs on the host before any launch.  A call that
+ *     returns an error has launched nothing and written nothing.
+ *   - txl_last_error() returns a thread-local message describing the last
+ *     failure on the calling thread.
+ *   - Strides are in ELEMENTS.  The innermost (feature) axis is always
+ *     contiguous.  Base pointers and every non-innermost stride must keep
+ *     16-byte alignment of each row.
+ *   - Floating-point tensors are TXL_BF16 (bfloat16) or TXL_F32.  Accumulation
+ *     is fp32 in every kernel; u, vb and lse are always fp32.
+ *   - Identical inputs give bitwise-identical outputs (no atomics, fixed
+ *     reduction orders).
+ */
+#ifndef TXL_H
+#define TXL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TXL_OK = 0,
+    TXL_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad stride/alignment        */
+    TXL_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. an unsupported dh)   */
+    TXL_ERR_ALIAS = 3,       /* an output overlaps an input that must stay intact    */
+    TXL_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned           */
+    TXL_ERR_HIP = 5          /* a HIP runtime call failed; see txl_last_error()      */
+} txl_status;
+
+typedef enum { TXL_F32 = 0, TXL_BF16 = 1 } txl_dtype;
+
+/* Library version string, e.g. "0.1.0". */
+const char *txl_version(void);
+/* Static description of a status code. */
+const char *txl_status_string(txl_status s);
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *txl_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Relative attention forward                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Shapes: B batch rows, H heads, L queries (current segment), M memory rows,
+ * K = M + L keys, dh = head width.
+ *   q     [B][H][L][dh]   strides q_stride  = {b, h, row}
+ *   k, v  [B][H][K][dh]   strides k_stride, v_stride
+ *   out   [B][H][L][dh]   strides o_stride
+ *   r_k   [H][K][dh]      strides r_stride  = {h, row}; row c holds the
+ *                         projected encoding of relative position K-1-c
+ *                         ([SRC] MemTransformerLM._forward orders positions
+ *                         K-1 .. 0)
+ *   u, vb [H][dh] fp32 contiguous: r_w_bias and r_r_bias
+ *   lse   [B][H][L] fp32 contiguous, optional (NULL = not written)
+ * q, k, v, r_k and out all have `dtype`. */
+typedef struct {
+    int B, H, L, M, dh;
+    int dtype;            /* txl_dtype */
+    float scale;          /* <= 0 selects 1/sqrt(dh) ([SRC] RelMultiHeadAttn) */
+    int splits;           /* key-range splits: 0 = automatic, 1 = none, n > 1 = n */
+    int64_t q_stride[3];
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+    int64_t r_stride[2];
+} txl_relattn_desc;
+
+/* Fills `desc` for densely packed tensors of the shapes above (splits = 0,
+ * scale = 1/sqrt(dh)).  Returns TXL_ERR_INVALID_ARG for a NULL desc. */
+txl_status txl_relattn_desc_init(txl_relattn_desc *desc, int B, int H, int L, int M, int dh,
+                                 txl_dtype dtype);
+
+/* Bytes of device workspace txl_relattn_fwd needs for `desc` (0 when the
+ * key range is not split).  *bytes is written on success. */
+txl_status txl_relattn_workspace_size(const txl_relattn_desc *desc, size_t *bytes);
+
+/* Segment-recurrent relative-position attention, forward.
+ *
+ * For each (b, h) and query i in [0, L), with keys j in [0, K) at positions
+ * j - M ([XL] "Batched Tensor Contract"; "Causal Mask With Memory"):
+ *   visible(i, j)  <=>  j <= i + M      (all memory, causal current segment)
+ *   s_ij = scale * ( (q_i + u) . k_j  +  (q_i + vb) . r_k[L-1-i+j] )
+ *   out_i = sum_j softmax_j(s_ij) v_j          over visible j
+ *   lse_i = log sum_j exp(s_ij)                over visible j
+ * This is [SRC] RelPartialLearnableMultiHeadAttn.forward from the score
+ * einsums to attn_vec (AC + rel_shift(BD), scale, masked_fill(-inf),
+ * softmax over keys, P.V) with the rel_shift done as direct distance
+ * indexing; [XL] "Relative Positional Encoding" gives the four-term form.
+ *
+ * dtype TXL_BF16: dh in {32, 64, 128}; TXL_F32: dh in {16, 32, 64}.
+ * L >= 1, M >= 0, B, H >= 1.  Workspace: at least
+ * txl_relattn_workspace_size() bytes, 256-byte aligned (may be NULL when
+ * that size is 0).  `out` must not overlap q, k, v or r_k (TXL_ERR_ALIAS). */
+txl_status txl_relattn_fwd(const txl_relattn_desc *desc, const void *q, const void *k, const void *v,
+                           const void *r_k, const float *u, const float *vb, void *out, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Memory update (Tail_M)                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* new_mem = cat([mem; h], seq)[beg:end] with end = M_cur + max(0, L - ext_len)
+ * and beg = max(0, end - mem_len), per batch row ([SRC]
+ * MemTransformerLM._update_mems; with ext_len = 0 this is [XL] Tail_M:
+ * the last mem_len rows of [mem; h]).  A bit-exact copy.
+ *   mem     [B][M_cur][d]  batch stride mem_bs (rows contiguous, row = d)
+ *   h       [B][L][d]      batch stride h_bs
+ *   new_mem [B][M_new][d]  batch stride new_bs, M_new = end - beg
+ * `mem` may be NULL iff M_cur == 0.  new_mem must not overlap mem or h
+ * (TXL_ERR_ALIAS): the update is out of place, so callers double-buffer.
+ * *M_new (host pointer, may be NULL) receives end - beg.
+ * dtype: TXL_BF16 or TXL_F32; d * element size must be a multiple of 16 bytes. */
+txl_status txl_mem_update(const void *mem, int M_cur, const void *h, int L, void *new_mem, int mem_len,
+                          int ext_len, int B, int d, int dtype, int64_t mem_bs, int64_t h_bs,
+                          int64_t new_bs, int *M_new, void *stream);
+
+/* The same update for n_buf independent buffers in ONE launch (the N+1
+ * per-layer memories of a layer stack, [XL] "Segment-Level Recurrence").
+ * mem, h and new_mem are HOST arrays of n_buf device pointers; all buffers
+ * share the scalar arguments.  1 <= n_buf <= 64. */
+txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, const void *const *h,
+                                  int L, void *const *new_mem, int mem_len, int ext_len, int B, int d,
+                                  int dtype, int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TXL_H */

@@ -1,0 +1,143 @@
+"""Host-side checks of libtxl.so that need no GPU: it loads, exports every
+function include/txl.h declares, and rejects bad arguments before launching
+anything (only failing calls are made here, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_xl_relative_rel_amd as txl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "txl.h")
+
+OK, EINVAL, EUNSUP, EALIAS, EWS = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(txl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = txl.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(txl.EXPORTED)
+
+
+def test_version_and_status_strings():
+    lib = txl.lib()
+    assert lib.txl_version().decode().count(".") == 2
+    for s in range(6):
+        assert lib.txl_status_string(s).decode()
+
+
+def _desc(B=2, H=2, L=8, M=4, dh=64, dtype=txl.BF16):
+    d = txl.RelAttnDesc()
+    assert txl.lib().txl_relattn_desc_init(ctypes.byref(d), B, H, L, M, dh, dtype) == OK
+    return d
+
+
+def test_desc_init_packs_dense_strides():
+    d = _desc(B=3, H=5, L=7, M=9, dh=32)
+    K = 16
+    assert list(d.q_stride) == [5 * 7 * 32, 7 * 32, 32]
+    assert list(d.k_stride) == [5 * K * 32, K * 32, 32]
+    assert list(d.r_stride) == [K * 32, 32]
+    assert abs(d.scale - 32 ** -0.5) < 1e-7
+
+
+FAKE = 1 << 30  # 16-byte aligned addresses, 1 GiB apart, never dereferenced
+
+
+def _fwd(d, q=FAKE, k=FAKE * 2, v=FAKE * 3, r=FAKE * 4, u=FAKE * 5, vb=FAKE * 6, out=FAKE * 7, lse=0, ws=0,
+         ws_bytes=0):
+    vp = ctypes.c_void_p
+    return txl.lib().txl_relattn_fwd(ctypes.byref(d) if d is not None else None, vp(q), vp(k), vp(v), vp(r), vp(u),
+                                     vp(vb), vp(out), vp(lse), vp(ws), ws_bytes, vp(0))
+
+
+def test_relattn_rejects_bad_arguments():
+    lib = txl.lib()
+    assert _fwd(None) == EINVAL
+    for field, val in (("L", 0), ("B", 0), ("M", -1), ("dtype", 7)):
+        d = _desc()
+        setattr(d, field, val)
+        assert _fwd(d) == EINVAL, field
+    assert _fwd(_desc(dh=48)) == EUNSUP
+    assert _fwd(_desc(dh=16, dtype=txl.BF16)) == EUNSUP
+    assert _fwd(_desc(dh=128, dtype=txl.F32)) == EUNSUP
+    assert b"dh" in lib.txl_last_error()
+    assert _fwd(_desc(), q=0) == EINVAL
+    assert _fwd(_desc(), k=FAKE * 2 + 8) == EINVAL          # misaligned base
+    d = _desc()
+    d.q_stride[2] = 65                                       # row breaks 16-byte alignment
+    assert _fwd(d) == EINVAL
+    d = _desc()
+    d.k_stride[2] = 32                                       # rows would overlap
+    assert _fwd(d) == EINVAL
+
+
+def test_relattn_rejects_aliasing():
+    d = _desc(B=1, H=1, L=8, M=0, dh=64)
+    assert _fwd(d, out=FAKE) == EALIAS                       # out == q
+    assert _fwd(d, out=FAKE + 64) == EALIAS                  # partial overlap with q
+    assert _fwd(d, lse=FAKE * 3 + 16) == EALIAS              # lse inside v
+
+
+def test_split_plan_needs_workspace():
+    d = _desc(B=1, H=16, L=128, M=1600, dh=64)               # long memory: split automatically
+    n = ctypes.c_size_t(0)
+    assert txl.lib().txl_relattn_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value > 0
+    assert _fwd(d) == EWS
+    assert _fwd(d, ws=FAKE * 16 + 16, ws_bytes=n.value) == EWS  # misaligned
+    assert _fwd(d, ws=FAKE * 16, ws_bytes=n.value - 1) == EWS
+    d3 = _desc(B=8, H=16, L=512, M=512, dh=64)               # enough blocks: no split
+    assert txl.lib().txl_relattn_workspace_size(ctypes.byref(d3), ctypes.byref(n)) == OK
+    assert n.value == 0
+    d3.splits = 4
+    assert txl.lib().txl_relattn_workspace_size(ctypes.byref(d3), ctypes.byref(n)) == OK
+    assert n.value >= 4 * 8 * 16 * 512 * 64 * 4
+
+
+def _mem(mem=FAKE, M_cur=8, h=FAKE * 2, L=8, new=FAKE * 3, mem_len=8, ext=0, B=2, d=32, dtype=txl.BF16,
+         mem_bs=None, h_bs=None, new_bs=None):
+    vp = ctypes.c_void_p
+    mem_bs = M_cur * d if mem_bs is None else mem_bs
+    h_bs = L * d if h_bs is None else h_bs
+    new_bs = mem_len * d if new_bs is None else new_bs
+    got = ctypes.c_int(-1)
+    s = txl.lib().txl_mem_update(vp(mem), M_cur, vp(h), L, vp(new), mem_len, ext, B, d, dtype, mem_bs, h_bs, new_bs,
+                                 ctypes.byref(got), vp(0))
+    return s
+
+
+def test_mem_update_rejects_bad_arguments():
+    assert _mem(mem=0) == EINVAL                 # M_cur > 0 needs mem
+    assert _mem(d=4) == EINVAL                   # 8-byte rows
+    assert _mem(B=0) == EINVAL
+    assert _mem(mem_len=-1) == EINVAL
+    assert _mem(h=FAKE * 2 + 2) == EINVAL        # misaligned
+    assert _mem(new=FAKE) == EALIAS              # in place over mem
+    assert _mem(new=FAKE * 2 + 64) == EALIAS     # overlaps h
+    assert _mem(h_bs=8) == EINVAL                # batch stride smaller than a batch row
+    vp = ctypes.c_void_p
+    arr = (vp * 1)(vp(FAKE))
+    got = ctypes.c_int()
+    assert txl.lib().txl_mem_update_batched(0, arr, 1, arr, 1, arr, 1, 0, 1, 32, txl.BF16, 32, 32, 32,
+                                            ctypes.byref(got), vp(0)) == EINVAL
+    assert txl.lib().txl_mem_update_batched(65, arr, 1, arr, 1, arr, 1, 0, 1, 32, txl.BF16, 32, 32, 32,
+                                            ctypes.byref(got), vp(0)) == EINVAL
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(txl, "_lib", None)
+    monkeypatch.setattr(txl, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        txl.lib()

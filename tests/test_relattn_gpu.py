@@ -1,0 +1,218 @@
+"""Parity of the HIP relative-attention kernel (through the C ABI) with the CPU
+oracle, plus probes whose answers are fixed by the method itself.
+
+Tolerances: fp32 path max |err| <= 1e-4; bf16 path (bf16 inputs, fp32
+accumulation, bf16 output) against the fp64 oracle on the same bf16 inputs:
+max |err| <= 2e-2 and mean |err| <= 2e-3.  Because the outputs of the
+benchmark-like shapes are small (|out| ~ 1e-2), the bf16 cases also bound the
+error relative to the output's RMS (<= 2%), which a wrong index cannot pass.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_xl_relative_rel_amd as txl
+from transformer_xl_relative_rel_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(DEV).to(dtype)
+
+
+def run_gpu(d, dtype, **kw):
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, r = (dev(d[x], td) for x in ("q", "k", "v", "r"))
+    u, vb = dev(d["u"], torch.float32), dev(d["vb"], torch.float32)
+    out, lse = txl.relattn_fwd(q, k, v, r, u, vb, want_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_close(got, want, dtype, what=""):
+    err = np.abs(got - want)
+    if dtype == "f32":
+        assert err.max() <= 1e-4, f"{what} max err {err.max():.3e}"
+    else:
+        rms = math.sqrt(float(np.mean(want ** 2)))
+        assert err.max() <= 2e-2, f"{what} max err {err.max():.3e}"
+        assert err.mean() <= 2e-3, f"{what} mean err {err.mean():.3e}"
+        assert err.mean() <= 0.02 * rms, f"{what} mean err {err.mean():.3e} vs rms {rms:.3e}"
+
+
+def config1_inputs():
+    """B=1, H=2, dh=16, L=8, M=8, fp32; every random value 0.5*N(0,1); r_k is
+    the sinusoid encoding of positions K-1..0 (d=32) times a random
+    projection, split into heads."""
+    B, H, L, M, dh = 1, 2, 8, 8, 16
+    K, d = M + L, H * dh
+    pe = oracle.pos_emb(K, d)                                   # [K, d]
+    W_r = synth.normal((H * dh, d), synth.STREAM["w_r"], 0.5)
+    r = (pe @ W_r.T).reshape(K, H, dh).transpose(1, 0, 2)       # [H, K, dh]
+    return synth.relattn_inputs(B, H, L, M, dh, dtype="f32", std=0.5, bias_std=0.5, r_k=r)
+
+
+def test_config1_fp32_full_parity():
+    log("case: config1 fp32 B1 H2 dh16 L8 M8")
+    d = config1_inputs()
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"])
+    got, glse = run_gpu(d, "f32")
+    check_close(got, want, "f32", "out")
+    assert np.abs(glse - wlse).max() <= 1e-4
+
+
+FP32_CASES = [
+    # B, H, L, M, dh, splits
+    (1, 1, 1, 0, 16, 0), (1, 2, 5, 0, 16, 0), (2, 3, 17, 3, 32, 0), (1, 2, 63, 1, 64, 0), (2, 4, 65, 64, 64, 0),
+    (1, 8, 100, 37, 32, 0), (2, 4, 130, 200, 64, 3), (1, 1, 7, 150, 16, 5), (8, 1, 33, 31, 64, 1), (1, 3, 64, 0, 64, 2),
+]
+
+
+@pytest.mark.parametrize("B,H,L,M,dh,splits", FP32_CASES)
+def test_fp32_parity_sweep(B, H, L, M, dh, splits):
+    log(f"case: fp32 B{B} H{H} L{L} M{M} dh{dh} splits{splits}")
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="f32", std=0.5, bias_std=0.5, seed=1111 + L * 7 + M)
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=8)
+    got, glse = run_gpu(d, "f32", splits=splits)
+    check_close(got, want, "f32", "out")
+    assert np.abs(glse - wlse).max() <= 1e-4
+
+
+BF16_CASES = [
+    (1, 2, 1, 0, 64, 0), (2, 2, 19, 5, 32, 0), (1, 4, 128, 128, 64, 0), (2, 8, 200, 77, 64, 0),
+    (1, 2, 96, 33, 128, 0), (2, 8, 256, 256, 64, 0), (1, 16, 128, 640, 64, 0), (1, 2, 70, 300, 64, 4),
+    (4, 8, 256, 128, 64, 1),
+]
+
+
+@pytest.mark.parametrize("B,H,L,M,dh,splits", BF16_CASES)
+def test_bf16_parity_sweep(B, H, L, M, dh, splits):
+    log(f"case: bf16 B{B} H{H} L{L} M{M} dh{dh} splits{splits}")
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16", seed=2222 + L + M)
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=8)
+    got, glse = run_gpu(d, "bf16", splits=splits)
+    check_close(got, want, "bf16", "out")
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+FULL = {
+    "cfg2_B8_H16_dh64_L512_M256": (8, 16, 512, 256, 64),
+    "cfg3_B8_H16_dh64_L512_M512": (8, 16, 512, 512, 64),
+    "cfg4_B1_H16_dh64_L128_M1600": (1, 16, 128, 1600, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_bf16_full_size_sampled_rows(name):
+    B, H, L, M, dh = FULL[name]
+    log(f"case: {name} sampled rows")
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
+    got, glse = run_gpu(d, "bf16")
+    rng = np.random.default_rng(5)
+    rows = [(0, 0, 0), (B - 1, H - 1, L - 1), (0, H - 1, L // 2)]
+    rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(L))) for _ in range(61)]
+    want = np.stack([oracle.relattn_row(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], b, h, i)[0] for b, h, i in rows])
+    wl = np.array([oracle.relattn_row(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], b, h, i)[1] for b, h, i in rows])
+    g = np.stack([got[b, h, i] for b, h, i in rows])
+    gl = np.array([glse[b, h, i] for b, h, i in rows])
+    check_close(g, want, "bf16", name)
+    assert np.abs(gl - wl).max() <= 2e-2
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("dtype,dh", [("f32", 16), ("bf16", 32), ("bf16", 64)])
+@pytest.mark.parametrize("L,M", [(8, 8), (5, 9), (3, 0)])
+def test_mask_probe(dtype, dh, L, M):
+    # q = u = vb = 0 and r = 0 make every visible score 0; v[j] = e_j shows which
+    # keys each query sees: out[i][j] = 1/(M+i+1) if j <= i+M else exactly 0.
+    log(f"case: mask probe {dtype} dh{dh} L{L} M{M}")
+    K = M + L
+    assert K <= dh
+    z = np.zeros
+    d = {"q": z((1, 1, L, dh)), "k": synth.normal((1, 1, K, dh), 2, 0.5), "v": np.eye(K, dh)[None, None],
+         "r": z((1, K, dh)), "u": z((1, dh)), "vb": z((1, dh))}
+    got, _ = run_gpu(d, dtype)
+    vis = oracle.visible_mask(L, M)
+    assert np.all((got[0, 0, :, :K] != 0) == vis)
+    for i in range(L):
+        np.testing.assert_allclose(got[0, 0, i, : i + M + 1], 1.0 / (i + M + 1), rtol=4e-3 if dtype == "bf16" else 1e-6)
+
+
+@pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("L,M,target", [(16, 16, 0), (40, 70, 5), (64, 64, 33), (100, 20, 1)])
+def test_distance_probe(dtype, dh, L, M, target):
+    # Only the position term is non-zero: vb = e_0 and r row c carries
+    # -beta * |distance(c) - target| in column 0, distance(c) = K-1-c.  Each
+    # query then attends (almost) only to the key at distance `target`,
+    # j = i + M - target, or to key 0 when that key does not exist; v[j] = e_(j mod dh)
+    # shows which key won.
+    log(f"case: distance probe {dtype} dh{dh} L{L} M{M} target{target}")
+    K = M + L
+    beta = 64.0
+    r = np.zeros((1, K, dh))
+    r[0, :, 0] = -beta * np.abs(np.arange(K - 1, -1, -1) - target)
+    vb = np.zeros((1, dh)); vb[0, 0] = 1.0
+    v = np.zeros((1, 1, K, dh)); v[0, 0, np.arange(K), np.arange(K) % dh] = 1.0
+    d = {"q": np.zeros((1, 1, L, dh)), "k": np.zeros((1, 1, K, dh)), "v": v, "r": r, "u": np.zeros((1, dh)), "vb": vb}
+    got, _ = run_gpu(d, dtype)
+    for i in range(L):
+        j = max(i + M - target, 0)
+        assert np.argmax(got[0, 0, i]) == j % dh, (i, j)
+        assert got[0, 0, i, j % dh] > 0.99
+
+
+def test_rows_sum_to_one_probe():
+    log("case: row-sum probe bf16")
+    d = synth.relattn_inputs(2, 4, 130, 70, 64, dtype="bf16")
+    d["v"] = np.ones_like(d["v"])
+    got, _ = run_gpu(d, "bf16")
+    assert np.abs(got - 1.0).max() <= 4e-3
+
+
+def test_strided_views_and_determinism():
+    # q, k, v as views into one interleaved [B, T, 3, H, dh] buffer; out into a
+    # [B, L, H, dh] buffer (the merged-heads layout).  Two runs are bitwise equal.
+    log("case: strided views + determinism")
+    B, H, L, M, dh = 2, 8, 96, 64, 64
+    K = M + L
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
+    buf = torch.zeros((B, K, 3, H, dh), dtype=torch.bfloat16, device=DEV)
+    buf[:, :, 1] = dev(d["k"], torch.bfloat16).permute(0, 2, 1, 3)
+    buf[:, :, 2] = dev(d["v"], torch.bfloat16).permute(0, 2, 1, 3)
+    buf[:, M:, 0] = dev(d["q"], torch.bfloat16).permute(0, 2, 1, 3)
+    q = buf[:, M:, 0].permute(0, 2, 1, 3)
+    k = buf[:, :, 1].permute(0, 2, 1, 3)
+    v = buf[:, :, 2].permute(0, 2, 1, 3)
+    r = dev(d["r"], torch.bfloat16)
+    u, vb = dev(d["u"], torch.float32), dev(d["vb"], torch.float32)
+    ob = torch.zeros((B, L, H, dh), dtype=torch.bfloat16, device=DEV)
+    out = ob.permute(0, 2, 1, 3)
+    txl.relattn_fwd(q, k, v, r, u, vb, out=out)
+    torch.cuda.synchronize()
+    first = ob.clone()
+    txl.relattn_fwd(q, k, v, r, u, vb, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ob)
+    want, _ = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=8)
+    check_close(out.float().cpu().numpy(), want, "bf16", "strided")
+
+
+def test_split_and_unsplit_agree():
+    log("case: split vs unsplit")
+    d = synth.relattn_inputs(1, 16, 128, 1600, 64, dtype="bf16")
+    a, la = run_gpu(d, "bf16", splits=1)
+    b, lb = run_gpu(d, "bf16", splits=0)
+    assert np.abs(a - b).max() <= 8e-3
+    assert np.abs(la - lb).max() <= 1e-4

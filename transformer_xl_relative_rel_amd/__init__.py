@@ -1,1 +1,196 @@
-"""MI355X-native Transformer-XL relative attention (placeholder until the binding lands)."""
+"""MI355X-native Transformer-XL segment-recurrent relative attention.
+
+A thin binding over the C ABI of ``libtxl.so`` (declared in include/txl.h).
+It only marshals arguments: torch supplies device memory and the current
+stream, every step of the computation runs in the library's HIP kernels.
+If the library is not built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "mem_update", "mem_update_batched",
+    "F32", "BF16", "EXPORTED",
+]
+
+F32, BF16 = 0, 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtxl.so")
+_lib = None
+
+# Every function declared in include/txl.h.
+EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
+            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update", "txl_mem_update_batched")
+
+
+class TxlError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"txl status {status}: {msg}")
+        self.status = status
+
+
+class RelAttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("M", ctypes.c_int),
+                ("dh", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("splits", ctypes.c_int),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+                ("o_stride", ctypes.c_int64 * 3), ("r_stride", ctypes.c_int64 * 2)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libtxl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(transformer_xl_relative_rel_amd/build.py)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(RelAttnDesc)
+    L.txl_version.restype = ctypes.c_char_p
+    L.txl_status_string.argtypes = [i]
+    L.txl_status_string.restype = ctypes.c_char_p
+    L.txl_last_error.restype = ctypes.c_char_p
+    L.txl_relattn_desc_init.argtypes = [dp, i, i, i, i, i, i]
+    L.txl_relattn_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    L.txl_relattn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.txl_mem_update.argtypes = [vp, i, vp, i, vp, i, i, i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
+    L.txl_mem_update_batched.argtypes = [i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, i,
+                                         i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
+    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update",
+                 "txl_mem_update_batched"):
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise TxlError(status, lib().txl_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _desc(q, k, r_k, out, v, scale, splits) -> RelAttnDesc:
+    B, H, L, dh = q.shape
+    K = k.shape[2]
+    d = RelAttnDesc()
+    _check(lib().txl_relattn_desc_init(ctypes.byref(d), B, H, L, K - L, dh, _dtype_code(q)))
+    d.scale = 0.0 if scale is None else float(scale)
+    d.splits = int(splits)
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name[0]}: the last axis must be contiguous")
+        getattr(d, name)[:] = list(t.stride()[:3])
+    if r_k.stride(-1) != 1:
+        raise ValueError("r_k: the last axis must be contiguous")
+    d.r_stride[:] = list(r_k.stride()[:2])
+    return d
+
+
+def relattn_workspace_size(q, k, splits: int = 0) -> int:
+    """Workspace bytes txl_relattn_fwd needs for these shapes."""
+    import torch
+    B, H, L, dh = q.shape
+    d = RelAttnDesc()
+    _check(lib().txl_relattn_desc_init(ctypes.byref(d), B, H, L, k.shape[2] - L, dh, _dtype_code(q)))
+    d.splits = int(splits)
+    n = ctypes.c_size_t(0)
+    _check(lib().txl_relattn_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, lse=None, want_lse: bool = False,
+                splits: int = 0, workspace=None, stream=None):
+    """Relative attention forward (txl_relattn_fwd).
+
+    q [B, H, L, dh]; k, v [B, H, M+L, dh]; r_k [H, M+L, dh] (row c = relative
+    position M+L-1-c); u, vb [H, dh] float32.  bf16 or float32 tensors on one
+    device; strided views are accepted when the last axis is contiguous.
+    Returns out (and lse [B, H, L] float32 when ``want_lse`` or ``lse`` is given).
+    """
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    for t in (u, vb) + ((lse,) if lse is not None else ()):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("u, vb and lse must be contiguous float32")
+    d = _desc(q, k, r_k, out, v, scale, splits)
+    need = ctypes.c_size_t(0)
+    _check(lib().txl_relattn_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+    if need.value and workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().txl_relattn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
+                                 _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def _new_len(M_cur: int, L: int, mem_len: int, ext_len: int) -> int:
+    end = M_cur + max(0, L - ext_len)
+    return end - max(0, end - mem_len)
+
+
+def mem_update(mem, h, mem_len: int, ext_len: int = 0, out=None, stream=None):
+    """Tail_M memory update (txl_mem_update): mem [B, M_cur, d] or None, h [B, L, d] -> [B, M_new, d]."""
+    import torch
+    B, L, d = h.shape
+    M_cur = 0 if mem is None else mem.shape[1]
+    M_new = _new_len(M_cur, L, mem_len, ext_len)
+    if out is None:
+        out = torch.empty((B, M_new, d), dtype=h.dtype, device=h.device)
+    for t in (mem, h, out):
+        if t is not None and t.numel() and (t.stride(-1) != 1 or t.stride(-2) != d):
+            raise ValueError("rows must be contiguous")
+    got = ctypes.c_int(-1)
+    _check(lib().txl_mem_update(_ptr(mem if M_cur else None), M_cur, _ptr(h), L, _ptr(out), mem_len, ext_len, B, d,
+                                _dtype_code(h), mem.stride(0) if M_cur else 0, h.stride(0), out.stride(0),
+                                ctypes.byref(got), _stream(stream)))
+    assert got.value == M_new
+    return out
+
+
+def mem_update_batched(mems, hs, mem_len: int, ext_len: int = 0, outs=None, stream=None):
+    """One launch updating every buffer (txl_mem_update_batched); all share shapes."""
+    import torch
+    n = len(hs)
+    B, L, d = hs[0].shape
+    M_cur = 0 if mems is None or mems[0] is None else mems[0].shape[1]
+    M_new = _new_len(M_cur, L, mem_len, ext_len)
+    if outs is None:
+        outs = [torch.empty((B, M_new, d), dtype=hs[0].dtype, device=hs[0].device) for _ in range(n)]
+    arr = ctypes.c_void_p * n
+    mp = arr(*[(m.data_ptr() if M_cur else 0) for m in (mems if M_cur else [None] * n)]) if M_cur else arr()
+    hp = arr(*[t.data_ptr() for t in hs])
+    op = arr(*[t.data_ptr() for t in outs])
+    got = ctypes.c_int(-1)
+    _check(lib().txl_mem_update_batched(n, mp, M_cur, hp, L, op, mem_len, ext_len, B, d, _dtype_code(hs[0]),
+                                        mems[0].stride(0) if M_cur else 0, hs[0].stride(0),
+                                        outs[0].stride(0) if M_new else 0, ctypes.byref(got), _stream(stream)))
+    return outs

@@ -1,0 +1,48 @@
+// Internal launch interface between the host API (txl_api.cpp) and the HIP
+// kernels.  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace txl {
+
+// Keys per staged tile of the fused attention kernel and waves per workgroup.
+constexpr int kBK = 64;
+constexpr int kWaves = 4;
+
+struct RelAttnArgs {
+    const void *q, *k, *v, *r;
+    const float *u, *vb;
+    void *out;
+    float *lse;
+    float *part_o;   // [nsplit][B*H][L][dh] unnormalised partial outputs (split path)
+    float *part_ml;  // [nsplit][B*H][L][2]  running max (log2 units) and denominator
+    int64_t qs[3], ks[3], vs[3], os[3], rs[2];
+    int B, H, L, M, K;
+    float c;          // scale * log2(e)
+    int nqb;          // query blocks of 16 * kWaves * rb rows
+    int nsplit;       // key-range splits (1 = normalise in the kernel)
+    int tiles_per_split;
+    int remap;        // 1: XCD-aware workgroup order (needs B*H % 8 == 0)
+};
+
+// rb = 16-row blocks per wave (1 or 2).  dtype: 0 = f32, 1 = bf16.
+bool relattn_supported(int dtype, int dh, int rb);
+hipError_t launch_relattn(const RelAttnArgs &a, int dtype, int dh, int rb, hipStream_t s);
+
+constexpr int kMaxMemBuffers = 64;
+
+struct MemUpdateArgs {
+    const unsigned char *mem[kMaxMemBuffers];
+    const unsigned char *h[kMaxMemBuffers];
+    unsigned char *dst[kMaxMemBuffers];
+    int n_buf;
+    int M_cur, beg, M_new, B;
+    int row_chunks;                 // 16-byte chunks per row
+    int64_t mem_bs, h_bs, new_bs;   // batch strides in bytes
+};
+
+hipError_t launch_mem_update(const MemUpdateArgs &a, hipStream_t s);
+
+}  // namespace txl
