@@ -36,18 +36,37 @@ def min_bytes(B, H, L, M, dh, es=2):
     return es * (2 * B * H * L * dh + 2 * B * H * K * dh + H * K * dh)
 
 
-def cpu_baseline(d, B, H, L, M, dh, heads=16):
+def cpu_baseline(d, B, H, L, M, dh, heads=None):
     """Time the oracle on a bounded sample: the first `heads` (b, h) units of
-    the workload, split over the host's cores (each head is independent)."""
+    the workload (default all of them, about 10-15 s of CPU time), split over
+    at most 16 host threads (each head is independent)."""
     import oracle
 
+    heads = B * H if heads is None else heads
     threads = min(os.cpu_count() or 1, 16, heads)
     t0 = time.perf_counter()
+    c0 = time.process_time()
     oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=threads, bh_range=(0, heads))
     dt = time.perf_counter() - t0
+    cpu_s = time.process_time() - c0
     f = flops_alg(B, H, L, M, dh) * heads / (B * H)
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {B * H} (b,h) heads of the same workload, fp64 scalar C, {dt:.1f} s"}
+    return {"value": round(f / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {B * H} (b,h) heads of the same workload, fp64 scalar C oracle, "
+                      f"{dt:.2f} s wall, {cpu_s:.1f} s CPU"}
+
+
+def recorded_traffic(kernel_src):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel source (sha256 match); else None."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "relattn_fwd_bf16_B8H16L512M512_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
 
 
 def main():
@@ -56,6 +75,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run one Tail_M copy of this many MiB (bigger than every cache) so that a "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE pass can calibrate its counters against known bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single GPU)",
@@ -88,6 +110,12 @@ def main():
             ev[1].record(stream)
         txl.mem_update(mem, h, M, out=new_mem, stream=stream)
 
+    if args.calib_copy_mib > 0:
+        rows = args.calib_copy_mib * 128            # rows of 4096 bf16 = 8 KiB
+        src = torch.empty((1, rows, 4096), dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = txl.mem_update(None, src, rows)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -113,7 +141,9 @@ def main():
                    "L": L, "M": M, "parallelism": "single-gpu"},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(os.path.join(ROOT, "transformer_xl_relative_rel_amd", "csrc",
+                                                              "relattn_fwd.hip")),
                      "kernel": "relattn_fwd_kernel<bf16,64,2>", "kernel_ms": round(attn_ms, 5)},
     }
     if not args.no_cpu:

@@ -214,5 +214,8 @@ def test_split_and_unsplit_agree():
     d = synth.relattn_inputs(1, 16, 128, 1600, 64, dtype="bf16")
     a, la = run_gpu(d, "bf16", splits=1)
     b, lb = run_gpu(d, "bf16", splits=0)
+    # The two paths round p to bf16 against different running maxima, so they
+    # agree to bf16 rounding, not bitwise; each is checked against the oracle
+    # elsewhere.
     assert np.abs(a - b).max() <= 8e-3
-    assert np.abs(la - lb).max() <= 1e-4
+    assert np.abs(la - lb).max() <= 1e-3
