@@ -143,8 +143,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(os.path.join(ROOT, "transformer_xl_relative_rel_amd", "csrc",
-                                                              "relattn_fwd.hip")),
-                     "kernel": "relattn_fwd_kernel<bf16,64,2>", "kernel_ms": round(attn_ms, 5)},
+                                                              "relattn_fwd_bf16.hip")),
+                     "kernel": "relattn_fwd_bf16_kernel<64>", "kernel_ms": round(attn_ms, 5)},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(d, B, H, L, M, dh)

@@ -31,6 +31,13 @@ struct RelAttnArgs {
 bool relattn_supported(int dtype, int dh, int rb);
 hipError_t launch_relattn(const RelAttnArgs &a, int dtype, int dh, int rb, hipStream_t s);
 
+// bf16 throughput kernel (dh = 64): query rows per workgroup, and launch.
+int relattn_bf16_rows_per_block();
+bool relattn_bf16_supported(int dh);
+hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s);
+// Key-range combine used by both kernels when nsplit > 1.
+hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s);
+
 constexpr int kMaxMemBuffers = 64;
 
 struct MemUpdateArgs {

@@ -472,14 +472,29 @@ hipError_t launch_one(const RelAttnArgs &a, hipStream_t s)
     hipLaunchKernelGGL((relattn_fwd_kernel<BF, DH, RB>), dim3(blocks), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const int rows_per_block = 256 / (DH / 4);
-    const int64_t rows = (int64_t)a.B * a.H * a.L;
-    hipLaunchKernelGGL((relattn_combine_kernel<BF, DH>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                       dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_relattn_combine(a, BF ? 1 : 0, DH, s);
 }
 
 }  // namespace
+
+hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s)
+{
+    const int64_t rows = (int64_t)a.B * a.H * a.L;
+    const int rows_per_block = 256 / (dh / 4);
+    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+    if (dtype == 1) {
+        if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), grid, dim3(256), 0, s, a);
+        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<true, 64>), grid, dim3(256), 0, s, a);
+        else if (dh == 128) hipLaunchKernelGGL((relattn_combine_kernel<true, 128>), grid, dim3(256), 0, s, a);
+        else return hipErrorInvalidValue;
+    } else {
+        if (dh == 16) hipLaunchKernelGGL((relattn_combine_kernel<false, 16>), grid, dim3(256), 0, s, a);
+        else if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), grid, dim3(256), 0, s, a);
+        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), grid, dim3(256), 0, s, a);
+        else return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 bool relattn_supported(int dtype, int dh, int rb)
 {

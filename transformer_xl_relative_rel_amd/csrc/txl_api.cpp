@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -55,6 +56,7 @@ bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Rows per wave block choice and key-range split of the attention kernel.
 struct Plan {
+    int fast;    // 1: bf16 throughput kernel, 0: generic kernel
     int rb, nqb, nsplit, tps;
     size_t ws_bytes;
 };
@@ -66,8 +68,15 @@ Plan plan_relattn(const txl_relattn_desc &d)
     Plan p{};
     const int BH = d.B * d.H;
     p.rb = 1;
-    if (d.dtype == TXL_BF16 && d.dh <= 64 && (int64_t)BH * ceil_div(d.L, 16 * txl::kWaves * 2) >= 256) p.rb = 2;
-    const int BQ = 16 * txl::kWaves * p.rb;
+    {
+        // the throughput kernel addresses each head's K, V and r rows with 32-bit byte offsets
+        const int64_t row = std::max(std::max(d.k_stride[2], d.v_stride[2]), d.r_stride[1]);
+        const int64_t span = ((int64_t)d.L + d.M + 64) * row * 2;
+        p.fast = (d.dtype == TXL_BF16 && txl::relattn_bf16_supported(d.dh) && span < ((int64_t)1 << 31)) ? 1 : 0;
+    }
+    if (!p.fast && d.dtype == TXL_BF16 && d.dh <= 64 && (int64_t)BH * ceil_div(d.L, 16 * txl::kWaves * 2) >= 256)
+        p.rb = 2;
+    const int BQ = p.fast ? txl::relattn_bf16_rows_per_block() : 16 * txl::kWaves * p.rb;
     p.nqb = ceil_div(d.L, BQ);
     const int ntile = ceil_div(d.L + d.M, txl::kBK);   // tiles of the longest query block
     int nsplit = d.splits;
@@ -224,7 +233,8 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     a.nsplit = p.nsplit;
     a.tiles_per_split = p.tps;
     a.remap = ((d->B * d->H) % 8 == 0) ? 1 : 0;
-    hipError_t e = txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
+    hipError_t e = p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
+                          : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn launch failed: %s", hipGetErrorString(e));
     return ok();
 }
