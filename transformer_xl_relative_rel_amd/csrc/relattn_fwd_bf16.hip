@@ -8,10 +8,10 @@
 //   s_ij = scale * ((q_i + u) . k_j + (q_i + vb) . r[L-1-i+j]),
 //   visible iff j <= i + M,  out_i = softmax_j(s_ij) . v_j.
 //
-// Work decomposition.  A workgroup is 2 waves and owns 128 query rows of one
-// (b, h); each wave owns 64 rows as four 16-query blocks.  Keys are walked in
-// tiles of 64.  Every K, V and r fragment read from LDS is used by several
-// blocks of the wave.
+// Work decomposition.  A workgroup is 8 waves (two per SIMD) and owns 256
+// query rows of one (b, h); each wave owns 32 rows as two 16-query blocks.
+// Keys are walked in tiles of 64.  Waves w and w + 4 share a SIMD and own
+// 32-query blocks s and 7 - s, whose key ranges add up to the same length.
 //
 // Everything is computed transposed (keys on MFMA rows, queries on lanes):
 //   T^T = R_band . (c (q + vb))^T - m   with c = scale * log2(e) folded into
@@ -28,12 +28,12 @@
 //   P comes out of the score MFMA in the B-operand layout of
 //   O^T += V^T . P^T  with V^T fragments read from row-major V through the
 //   transposing LDS read; the denominator is one more MFMA against ones.
-// The four blocks of a wave are software-pipelined: the softmax of block b
-// sits in one basic block with the band and content MFMAs of block b+1 and the
-// P.V MFMAs of block b, so the compiler can overlap VALU and MFMA work.
+// The two blocks of a wave are software-pipelined: the softmax of block 0
+// sits in one basic block with the band and content MFMAs of block 1 and the
+// P.V MFMAs of block 0.
 //
-// LDS: double-buffered K and V tiles, a 256-row ring of r rows (tile kt uses
-// 192 rows; the 64 rows of tile kt+1 go into the free quarter), one skew buffer
+// LDS: double-buffered K and V tiles, a ring of r rows (a tile uses 320 rows;
+// the 64 rows the next tile adds go into the free quarter), one skew buffer
 // per wave.  Tiles move HBM -> LDS with direct-to-LDS loads issued one tile
 // ahead; rows are 16-byte chunks with an XOR swizzle so that the 16 lanes of a
 // fragment read hit distinct banks.
@@ -109,12 +109,30 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Direct HBM -> LDS load of 16 bytes per lane through a buffer resource: lane
-// l of the wave writes lds_base + 16 l.  Byte offsets at or past the
-// resource's size (negative ones included, as unsigned) read zeros.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, u32x4 *lds_base)
+// l of the wave writes LDS byte address lds + 16 l.  Byte offsets at or past
+// the resource's size (negative ones included, as unsigned) read zeros.
+// Written as inline assembly so that the compiler does not track the load:
+// its own tracking of direct-to-LDS loads makes it wait for them before any
+// LDS read it cannot prove disjoint, which defeats the prefetch.  The caller
+// waits (s_waitcnt vmcnt(0) and a barrier) before anything reads the target.
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(LDS_AS char *)(LDS_AS void *)lds_base, 16, voff, 0,
-                                             0, 0);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(LDS_AS const void *)p;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -136,7 +154,7 @@ struct State {
     bf16x8 qu[RB][NKK], qv[RB][NKK];   // c (q + u), c (q + vb): B operands, lane (g, n) = query n
     f32x4 o[RB][NDT];                   // O^T accumulators (unnormalised)
     f32x4 lsum[RB];                     // softmax denominators (all 4 entries equal)
-    f32x4 mneg[RB];                     // -m broadcast: initial accumulator of the band MFMA
+    float mneg[RB];                     // -m: initial accumulator value of the band MFMA
     float mref[RB];                     // running max (log2 units)
 };
 
@@ -147,15 +165,16 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
     const int d0 = 4 * g - n;   // key offset minus query offset of this lane
 
-    // ---- fragments shared by the blocks of the wave
-    bf16x8 kf[NT][NKK];
+    // K fragments (A operands of the content MFMA)
+    auto load_k = [&](bf16x8 (&kf)[NT][NKK]) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        const int krow = 16 * tt + n;
+        for (int tt = 0; tt < NT; ++tt) {
+            const int krow = 16 * tt + n;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            kf[tt][kk] = __builtin_bit_cast(bf16x8, t.sk[krow * CPR + ((4 * kk + g) ^ swz_k(krow))]);
-    }
+            for (int kk = 0; kk < NKK; ++kk)
+                kf[tt][kk] = __builtin_bit_cast(bf16x8, t.sk[krow * CPR + ((4 * kk + g) ^ swz_k(krow))]);
+        }
+    };
     // V^T fragments (A operands of P.V), read through the transposing LDS read
     auto load_v = [&](bf16x8 (&vf)[NT / 2][NDT]) {
         LDS_AS char *vb = (LDS_AS char *)(LDS_AS void *)t.sv;
@@ -190,24 +209,32 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
 
     // band MFMA of block rb (wave band tiles RB-1-rb .. RB-1-rb+NT) and skew into LDS
     auto stage_a = [&](int rb) {
+        // all fragment reads first, then the five chains interleaved, then the skew writes
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) load_r(bt + (RB - 1) - rb);
+        const f32x4 m4 = {st.mneg[rb], st.mneg[rb], st.mneg[rb], st.mneg[rb]};
+        f32x4 acc[NBT];
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + (RB - 1) - rb][0], st.qv[rb][0], m4);
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk)
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + (RB - 1) - rb][kk], st.qv[rb][kk], acc[bt]);
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
-            const int wb = bt + (RB - 1) - rb;
-            load_r(wb);
-            f32x4 acc = st.mneg[rb];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = mfma(rf[wb][kk], st.qv[rb][kk], acc);
             // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
             float *dst = t.skw + n * (SROW + 1) + 16 * bt + 4 * g + 1;
-            dst[0] = acc[0];
-            dst[1] = acc[1];
-            dst[2] = acc[2];
-            dst[3] = acc[3];
+            dst[0] = acc[bt][0];
+            dst[1] = acc[bt][1];
+            dst[2] = acc[bt][2];
+            dst[3] = acc[bt][3];
         }
         wave_lds_sync();
     };
     // content MFMA of block rb on top of the skewed band values
     auto stage_b = [&](int rb) {
+        bf16x8 kf[NT][NKK];
+        load_k(kf);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             f32x4 acc = *reinterpret_cast<const f32x4 *>(t.skw + n * SROW + 16 + 16 * tt + 4 * g);
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.mneg[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.mneg[rb] = 0.f;
         st.mref[rb] = 0.f;
     }
 
@@ -375,18 +402,20 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
     const int kch = ((tid & (CPR - 1)) ^ swz_k(lrow)) * 16;
     const int vch = ((tid & (CPR - 1)) ^ swz_v(lrow)) * 16;
     const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
-    u32x4 *const kdst0 = &sk[0][wave * 64], *const kdst1 = &sk[1][wave * 64];
-    u32x4 *const vdst0 = &sv[0][wave * 64], *const vdst1 = &sv[1][wave * 64];
+    const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][wave * 64]));
+    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][wave * 64]));
+    const uint32_t sr_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[wave * 64]));
     auto load_kv = [&](int kt) {
         const int row = kt * BK + lrow;
-        load_lds16(krs, (uint32_t)(row * krow_b + kch), (kt & 1) ? kdst1 : kdst0);
-        load_lds16(vrs, (uint32_t)(row * vrow_b + vch), (kt & 1) ? vdst1 : vdst0);
+        const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
+        load_lds16(krs, (uint32_t)(row * krow_b + kch), sk_base + boff);
+        load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + boff);
     };
     // ring quarter t % NQ holds r rows c_base + 64 t .. +63 (the swizzle only
     // depends on the row within the quarter)
     auto load_r_quarter = [&](int t) {
         const int row = c_base + 64 * t + lrow;
-        load_lds16(rrs, (uint32_t)(row * rrow_b + kch), &sr[(t % NQ) * TILE_CH + wave * 64]);
+        load_lds16(rrs, (uint32_t)(row * rrow_b + kch), sr_base + (uint32_t)(t % NQ) * (TILE_CH * 16));
     };
 
     if (kt0 < kt1) {
@@ -418,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
             if (j0 + BK - 1 > wq0 + M) tile_body<true>(st, t, g, n);
             else tile_body<false>(st, t, g, n);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
     }
 
