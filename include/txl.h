@@ -141,6 +141,56 @@ txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, 
                                   int dtype, int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new,
                                   void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Decoder layer (relative attention + post-LayerNorm position-wise FF)     */
+/* ------------------------------------------------------------------------ */
+
+/* One RelPartialLearnableDecoderLayer forward with pre_lnorm = False and
+ * identity dropout ([SRC] RelPartialLearnableMultiHeadAttn.forward,
+ * PositionwiseFF.forward, MemTransformerLM._forward), for B batch rows of a
+ * segment of L tokens with M_cur rows of memory (K = M_cur + L):
+ *   pos    = sinusoid of positions K-1 .. 0      ([SRC] PositionalEmbedding:
+ *            sin in the first d/2 columns, cos in the rest, 10000^(-2t/d))
+ *   r_k    = pos W_r^T                            [K][H*dh]
+ *   q      = h W_q^T,  [k; v] = [mem; h] [W_k; W_v]^T   (W_qkv = [W_q; W_k; W_v])
+ *   attn   = txl_relattn_fwd over the H heads (rectangular mem + causal mask)
+ *   x      = LN1(h + attn W_o^T)
+ *   out    = LN2(x + W2 relu(W1 x + b1) + b2)
+ * LayerNorm uses the biased variance and eps ([SRC] nn.LayerNorm(d_model)).
+ *
+ * Tensors (device, caller-owned, dense, 16-byte aligned):
+ *   h_in, h_out [B][L][d] bf16;  mem [B][M_cur][d] bf16 (NULL iff M_cur == 0)
+ *   weights: bf16 matrices in nn.Linear [out][in] layout, fp32 vectors.
+ *   u, vb [H][dh] fp32 (r_w_bias, r_r_bias).
+ * Sizes: d, H*dh and d_inner multiples of 8; d even and <= 4096; dh in
+ * {32, 64, 128}.  h_out must not overlap any input, weight or the workspace
+ * (TXL_ERR_ALIAS).  Workspace: txl_layer_workspace_size() bytes, 256-byte
+ * aligned.  Intermediates are rounded to bf16 where they feed a GEMM or the
+ * attention kernel and kept in fp32 where they feed a LayerNorm. */
+typedef struct {
+    int B, L, d_model, n_head, d_head, d_inner;
+    float ln_eps;      /* <= 0 selects 1e-5 */
+} txl_layer_desc;
+
+typedef struct {
+    const void *W_qkv;                  /* [3*H*dh][d]  bf16 */
+    const void *W_r;                    /* [H*dh][d]    bf16 */
+    const void *W_o;                    /* [d][H*dh]    bf16 */
+    const float *ln1_g, *ln1_b;         /* [d]          fp32 */
+    const void *W1;                     /* [d_inner][d] bf16 */
+    const float *b1;                    /* [d_inner]    fp32 (NULL = zero) */
+    const void *W2;                     /* [d][d_inner] bf16 */
+    const float *b2;                    /* [d]          fp32 (NULL = zero) */
+    const float *ln2_g, *ln2_b;         /* [d]          fp32 */
+} txl_layer_weights;
+
+/* Workspace bytes of txl_layer_fwd for `desc` and M_cur memory rows. */
+txl_status txl_layer_workspace_size(const txl_layer_desc *desc, int M_cur, size_t *bytes);
+
+txl_status txl_layer_fwd(const txl_layer_desc *desc, const txl_layer_weights *w, const void *h_in,
+                         const void *mem, int M_cur, const float *u, const float *vb, void *h_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "mem_update", "mem_update_batched",
-    "F32", "BF16", "EXPORTED",
+    "layer_fwd", "layer_workspace_size", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
 
 F32, BF16 = 0, 1
@@ -22,7 +22,11 @@ _lib = None
 
 # Every function declared in include/txl.h.
 EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
-            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update", "txl_mem_update_batched")
+            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update", "txl_mem_update_batched",
+            "txl_layer_workspace_size", "txl_layer_fwd")
+
+# Weight names of one decoder layer, in the order of txl_layer_weights.
+LAYER_KEYS = ("W_qkv", "W_r", "W_o", "ln1_g", "ln1_b", "W1", "b1", "W2", "b2", "ln2_g", "ln2_b")
 
 
 class TxlError(RuntimeError):
@@ -36,6 +40,15 @@ class RelAttnDesc(ctypes.Structure):
                 ("dh", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("splits", ctypes.c_int),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
                 ("o_stride", ctypes.c_int64 * 3), ("r_stride", ctypes.c_int64 * 2)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("L", ctypes.c_int), ("d_model", ctypes.c_int), ("n_head", ctypes.c_int),
+                ("d_head", ctypes.c_int), ("d_inner", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in LAYER_KEYS]
 
 
 def lib_path() -> str:
@@ -63,8 +76,11 @@ def lib():
     L.txl_mem_update.argtypes = [vp, i, vp, i, vp, i, i, i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     L.txl_mem_update_batched.argtypes = [i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, i,
                                          i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
+    ldp = ctypes.POINTER(LayerDesc)
+    L.txl_layer_workspace_size.argtypes = [ldp, i, ctypes.POINTER(sz)]
+    L.txl_layer_fwd.argtypes = [ldp, ctypes.POINTER(LayerWeights), vp, vp, i, vp, vp, vp, vp, sz, vp]
     for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update",
-                 "txl_mem_update_batched"):
+                 "txl_mem_update_batched", "txl_layer_workspace_size", "txl_layer_fwd"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -194,3 +210,43 @@ def mem_update_batched(mems, hs, mem_len: int, ext_len: int = 0, outs=None, stre
                                         mems[0].stride(0) if M_cur else 0, hs[0].stride(0),
                                         outs[0].stride(0) if M_new else 0, ctypes.byref(got), _stream(stream)))
     return outs
+
+
+def _layer_desc(h_in, w, n_head: int, d_head: int, eps: float) -> LayerDesc:
+    B, L, d = h_in.shape
+    return LayerDesc(B, L, d, n_head, d_head, w["W1"].shape[0], eps)
+
+
+def layer_workspace_size(h_in, w, n_head: int, d_head: int, M_cur: int, eps: float = 1e-5) -> int:
+    """Workspace bytes txl_layer_fwd needs."""
+    n = ctypes.c_size_t(0)
+    desc = _layer_desc(h_in, w, n_head, d_head, eps)
+    _check(lib().txl_layer_workspace_size(ctypes.byref(desc), M_cur, ctypes.byref(n)))
+    return n.value
+
+
+def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, *, eps: float = 1e-5, out=None, workspace=None,
+              stream=None):
+    """One post-LN decoder layer (txl_layer_fwd).
+
+    h_in [B, L, d] bf16; mem [B, M_cur, d] bf16 or None; w maps LAYER_KEYS to
+    tensors (matrices bf16 in nn.Linear [out, in] layout, vectors float32, b1 /
+    b2 may be None); u, vb [H, dh] float32.  Returns h_out [B, L, d] bf16.
+    """
+    import torch
+    M_cur = 0 if mem is None else mem.shape[1]
+    desc = _layer_desc(h_in, w, n_head, d_head, eps)
+    if out is None:
+        out = torch.empty_like(h_in)
+    for t in [h_in, out] + ([mem] if M_cur else []) + [w[k] for k in LAYER_KEYS if w.get(k) is not None]:
+        if not t.is_contiguous():
+            raise ValueError("layer tensors must be contiguous")
+    need = ctypes.c_size_t(0)
+    _check(lib().txl_layer_workspace_size(ctypes.byref(desc), M_cur, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=h_in.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lw = LayerWeights(*[(w[k].data_ptr() if w.get(k) is not None else None) for k in LAYER_KEYS])
+    _check(lib().txl_layer_fwd(ctypes.byref(desc), ctypes.byref(lw), _ptr(h_in), _ptr(mem if M_cur else None), M_cur,
+                               _ptr(u), _ptr(vb), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out

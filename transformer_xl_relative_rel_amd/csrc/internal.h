@@ -52,4 +52,11 @@ struct MemUpdateArgs {
 
 hipError_t launch_mem_update(const MemUpdateArgs &a, hipStream_t s);
 
+// Decoder-layer helpers (layer_kernels.hip).  Tensors are bf16 (uint16_t) or fp32.
+int layer_norm_max_width();
+hipError_t launch_pos_emb(uint16_t *out, int K, int d, int clamp_len, hipStream_t s);
+hipError_t launch_bias_relu(const float *x, const float *b, uint16_t *y, int64_t N, int n, hipStream_t s);
+hipError_t launch_add_layer_norm(const uint16_t *res, const float *add, const float *bias, const float *g,
+                                 const float *beta, uint16_t *out, int64_t N, int d, float eps, hipStream_t s);
+
 }  // namespace txl

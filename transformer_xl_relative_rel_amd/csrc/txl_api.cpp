@@ -132,6 +132,15 @@ txl_status check_desc(const txl_relattn_desc *d)
 
 }  // namespace
 
+namespace txl {
+// Records the message of the calling thread's last call (shared with txl_layer.cpp).
+txl_status set_error(txl_status s, const char *msg)
+{
+    g_last_error = msg;
+    return s;
+}
+}  // namespace txl
+
 extern "C" {
 
 const char *txl_version(void) { return "0.1.0"; }
