@@ -62,6 +62,9 @@ def _load():
                                               _D, _D, _D, _D, _D, _D, _D, _D, _I, _I]
         lib.txo_relattn_row.argtypes = [_I, _I, _I, _I, ctypes.c_double, _I, _I, _I,
                                         _D, _D, _D, _D, _D, _D, _D, _D]
+        lib.txo_relattn_fwd_vis_range.argtypes = [_I, _I, _I, _I, _I, ctypes.c_double, _I,
+                                                  ctypes.POINTER(_I)] + [_D] * 8 + [_I, _I]
+        lib.txo_relattn_row_vis.argtypes = [_I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _I] + [_D] * 8
         lib.txo_mem_update.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I, _I, _I, _I, _I64, _I64, _I64]
         lib.txo_pos_emb.argtypes = [_I, _I, _I, _D]
         lib.txo_linear.argtypes = [_I, _I, _I, _D, _D, _D, _D]
@@ -69,6 +72,7 @@ def _load():
         lib.txo_layer_fwd.argtypes = [_I] * 7 + [_D] * 15 + [ctypes.c_double, _D]
         for name in ("txo_visible_mask", "txo_visible_mask_same_length", "txo_rel_shift",
                      "txo_relattn_scores", "txo_relattn_fwd_range", "txo_relattn_row",
+                     "txo_relattn_fwd_vis_range", "txo_relattn_row_vis",
                      "txo_mem_update", "txo_pos_emb", "txo_linear", "txo_layer_norm", "txo_layer_fwd"):
             getattr(lib, name).restype = _I
         _lib = lib
@@ -126,7 +130,8 @@ def relattn_scores(q, k, r, u, vb, M: int, scale: float | None = None, literal: 
 
 
 def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = False,
-                threads: int = 1, bh_range: tuple[int, int] | None = None):
+                threads: int = 1, bh_range: tuple[int, int] | None = None,
+                same_length: int = 0, mem_valid=None):
     """Relative attention over all heads.
 
     q [B, H, L, dh]; k, v [B, H, M+L, dh]; r [H, M+L, dh]; u, vb [H, dh].
@@ -134,6 +139,10 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
     splits the independent (b, h) heads across Python threads (the C call
     releases the GIL); ``bh_range`` restricts the work to a slice of the
     flattened (b, h) index (the other rows of the result stay zero).
+    ``same_length`` > 0 applies the same_length mask of [SRC]
+    MemTransformerLM._forward with that mem_len; ``mem_valid`` ([B] ints in
+    [0, M]) hides the oldest M - mem_valid[b] memory rows of batch row b
+    (per-row memory reset).  Both use the direct score form.
     """
     q, k, v, r, u, vb = map(_f64, (q, k, v, r, u, vb))
     B, H, L, dh = q.shape
@@ -147,9 +156,20 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
     lo, hi = (0, B * H) if bh_range is None else bh_range
     sc = 0.0 if scale is None else float(scale)
     args = (_p(q), _p(k), _p(v), _p(r), _p(u), _p(vb), _p(out), _p(lse))
+    variant = same_length > 0 or mem_valid is not None
+    assert not (variant and literal), "the mask variants use the direct form"
+    mv = None
+    if mem_valid is not None:
+        mv = np.ascontiguousarray(np.asarray(mem_valid, dtype=np.int32))
+        assert mv.shape == (B,)
 
     def run(a, b):
-        _check(lib.txo_relattn_fwd_range(B, H, L, M, dh, sc, int(literal), *args, a, b), "relattn_fwd")
+        if variant:
+            mvp = mv.ctypes.data_as(ctypes.POINTER(_I)) if mv is not None else None
+            _check(lib.txo_relattn_fwd_vis_range(B, H, L, M, dh, sc, int(same_length), mvp, *args, a, b),
+                   "relattn_fwd_vis")
+        else:
+            _check(lib.txo_relattn_fwd_range(B, H, L, M, dh, sc, int(literal), *args, a, b), "relattn_fwd")
 
     if threads <= 1 or hi - lo <= 1:
         run(lo, hi)
@@ -164,16 +184,25 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
     return out, lse
 
 
-def relattn_row(q, k, v, r, u, vb, b: int, h: int, i: int, scale: float | None = None):
-    """Output row out[b, h, i, :] and lse[b, h, i], computed alone (for sampled checks)."""
+def relattn_row(q, k, v, r, u, vb, b: int, h: int, i: int, scale: float | None = None,
+                same_length: int = 0, mem_valid: int | None = None):
+    """Output row out[b, h, i, :] and lse[b, h, i], computed alone (for sampled checks).
+    ``same_length`` and ``mem_valid`` (this row's valid memory count) as in relattn_fwd."""
     q, k, v, r, u, vb = map(_f64, (q, k, v, r, u, vb))
     B, H, L, dh = q.shape
     M = k.shape[2] - L
     row = np.empty(dh, dtype=np.float64)
     lse = np.empty(1, dtype=np.float64)
-    _check(_load().txo_relattn_row(H, L, M, dh, 0.0 if scale is None else scale, b, h, i,
-                                   _p(q), _p(k), _p(v), _p(r), _p(u), _p(vb), _p(row), _p(lse)),
-           "relattn_row")
+    sc = 0.0 if scale is None else scale
+    if same_length > 0 or mem_valid is not None:
+        mvb = M if mem_valid is None else int(mem_valid)
+        _check(_load().txo_relattn_row_vis(H, L, M, dh, sc, int(same_length), mvb, b, h, i,
+                                           _p(q), _p(k), _p(v), _p(r), _p(u), _p(vb), _p(row), _p(lse)),
+               "relattn_row_vis")
+    else:
+        _check(_load().txo_relattn_row(H, L, M, dh, sc, b, h, i,
+                                       _p(q), _p(k), _p(v), _p(r), _p(u), _p(vb), _p(row), _p(lse)),
+               "relattn_row")
     return row, float(lse[0])
 
 

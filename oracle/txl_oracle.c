@@ -257,6 +257,116 @@ int txo_relattn_fwd(int B, int H, int L, int M, int dh, double scale, int litera
     return txo_relattn_fwd_range(B, H, L, M, dh, scale, literal, q, k, v, r, u, vb, out, lse, 0, B * H);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Mask variants: same_length and per-row memory validity                   */
+/* ------------------------------------------------------------------------ */
+
+/* Visibility of one batch row.  same_len > 0 selects the same_length mask of
+ * [SRC] MemTransformerLM._forward with mem_len = same_len (see
+ * txo_visible_mask_same_length); otherwise the plain triu(1 + M) mask.
+ * mvalid is the number of valid memory rows of this batch row: after a
+ * document boundary only the newest rows of the memory belong to the row's
+ * own stream ([XL] "Batched Streams": the reset is per row), so keys
+ * j < M - mvalid are hidden as well.  mvalid = M hides nothing. */
+static int head_visible(int L, int M, int same_len, int mvalid, unsigned char *vis)
+{
+    int K = M + L;
+    int rc = same_len > 0 ? txo_visible_mask_same_length(L, M, same_len, vis) : txo_visible_mask(L, M, vis);
+    if (rc != TXO_OK) return rc;
+    for (int i = 0; i < L; ++i)
+        for (int j = 0; j < M - mvalid; ++j) vis[(size_t)i * K + j] = 0;
+    return TXO_OK;
+}
+
+/* Direct-form scores of one head with an explicit visibility mask. */
+static void head_scores_vis(int L, int M, int dh, double scale, const double *q, const double *k,
+                            const double *r, const double *u, const double *vb, const unsigned char *vis,
+                            double *S)
+{
+    int K = M + L;
+    for (int i = 0; i < L; ++i)
+        for (int j = 0; j < K; ++j) {
+            if (!vis[(size_t)i * K + j]) { S[(size_t)i * K + j] = -INFINITY; continue; }
+            int c = L - 1 - i + j;
+            double ac = 0.0, bd = 0.0;
+            for (int e = 0; e < dh; ++e) {
+                double qe = q[(size_t)i * dh + e];
+                ac += (qe + u[e]) * k[(size_t)j * dh + e];
+                bd += (qe + vb[e]) * r[(size_t)c * dh + e];
+            }
+            S[(size_t)i * K + j] = (ac + bd) * scale;
+        }
+}
+
+/* txo_relattn_fwd_range with the mask variants above.  same_len: 0 = off.
+ * mem_valid: [B] valid memory rows per batch row, each in [0, M]; NULL means
+ * all M rows are valid. */
+int txo_relattn_fwd_vis_range(int B, int H, int L, int M, int dh, double scale, int same_len,
+                              const int *mem_valid, const double *q, const double *k, const double *v,
+                              const double *r, const double *u, const double *vb, double *out, double *lse,
+                              int bh_begin, int bh_end)
+{
+    if (B < 1 || H < 1 || L < 1 || M < 0 || dh < 1 || same_len < 0) return TXO_EINVAL;
+    if (bh_begin < 0 || bh_end > B * H || bh_begin > bh_end) return TXO_EINVAL;
+    if (mem_valid)
+        for (int b = 0; b < B; ++b)
+            if (mem_valid[b] < 0 || mem_valid[b] > M) return TXO_EINVAL;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)dh);
+    int K = M + L;
+    double *S = (double *)malloc((size_t)L * K * sizeof(double));
+    unsigned char *vis = (unsigned char *)malloc((size_t)L * K);
+    if (!S || !vis) { free(S); free(vis); return TXO_ENOMEM; }
+    int rc = TXO_OK;
+    for (int bh = bh_begin; bh < bh_end && rc == TXO_OK; ++bh) {
+        int b = bh / H, h = bh % H;
+        rc = head_visible(L, M, same_len, mem_valid ? mem_valid[b] : M, vis);
+        if (rc != TXO_OK) break;
+        head_scores_vis(L, M, dh, scale, q + (size_t)bh * L * dh, k + (size_t)bh * K * dh, r + (size_t)h * K * dh,
+                        u + (size_t)h * dh, vb + (size_t)h * dh, vis, S);
+        head_softmax_pv(L, K, dh, S, v + (size_t)bh * K * dh, out + (size_t)bh * L * dh,
+                        lse ? lse + (size_t)bh * L : NULL);
+    }
+    free(S);
+    free(vis);
+    return rc;
+}
+
+/* One query row with the mask variants (sampled checks at full size). */
+int txo_relattn_row_vis(int H, int L, int M, int dh, double scale, int same_len, int mvalid, int b, int h, int i,
+                        const double *q, const double *k, const double *v, const double *r, const double *u,
+                        const double *vb, double *row_out, double *row_lse)
+{
+    if (H < 1 || L < 1 || M < 0 || dh < 1 || i < 0 || i >= L || h < 0 || h >= H || b < 0) return TXO_EINVAL;
+    if (same_len < 0 || mvalid < 0 || mvalid > M) return TXO_EINVAL;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)dh);
+    int K = M + L;
+    size_t bh = (size_t)b * H + h;
+    unsigned char *vis = (unsigned char *)malloc((size_t)L * K);
+    double *s = (double *)malloc((size_t)K * sizeof(double));
+    if (!vis || !s) { free(vis); free(s); return TXO_ENOMEM; }
+    int rc = head_visible(L, M, same_len, mvalid, vis);
+    if (rc == TXO_OK) {
+        /* the row's scores alone: the first query row of the slice is row i */
+        const double *qi = q + (bh * L + i) * dh;
+        const double *kh = k + bh * K * dh, *rh = r + (size_t)h * K * dh;
+        const double *uh = u + (size_t)h * dh, *wh = vb + (size_t)h * dh;
+        for (int j = 0; j < K; ++j) {
+            if (!vis[(size_t)i * K + j]) { s[j] = -INFINITY; continue; }
+            int c = L - 1 - i + j;
+            double ac = 0.0, bd = 0.0;
+            for (int e = 0; e < dh; ++e) {
+                ac += (qi[e] + uh[e]) * kh[(size_t)j * dh + e];
+                bd += (qi[e] + wh[e]) * rh[(size_t)c * dh + e];
+            }
+            s[j] = (ac + bd) * scale;
+        }
+        head_softmax_pv(1, K, dh, s, v + bh * K * dh, row_out, row_lse);
+    }
+    free(vis);
+    free(s);
+    return rc;
+}
+
 /* One output element, for sampled checks at full size: out[b][h][i][e] and
  * lse[b][h][i] for a single query row i (all e written to row_out[dh]). */
 int txo_relattn_row(int H, int L, int M, int dh, double scale, int b, int h, int i,

@@ -31,6 +31,9 @@ MUTATIONS = [
     ("pos_emb_interleaved", "out[(size_t)c * demb + half + t] = cos(p * inv_freq);",
      "out[(size_t)c * demb + half + t] = cos(p * inv_freq + 1e-3);"),
     ("ln_unbiased_var", "var /= d;", "var /= (d - 1);"),
+    ("mem_valid_off_by_one", "for (int j = 0; j < M - mvalid; ++j) vis",
+     "for (int j = 0; j < M - mvalid + 1 && j < K; ++j) vis"),
+    ("same_length_shift", "int lower = (j - i) <= -shift;", "int lower = (j - i) < -shift;"),
 ]
 
 PINS = [
@@ -44,6 +47,8 @@ PINS = [
     lambda: pins.test_layer_matches_torch_third_opinion(5),
     pins.test_rows_sum_to_one,
     pins.test_m0_zero_position_is_causal_sdpa,
+    lambda: pins.test_mem_valid_equals_truncated_memory(3),
+    lambda: pins.test_same_length_rows_are_windows(6, 4, 4),
 ]
 
 

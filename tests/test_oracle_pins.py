@@ -78,6 +78,79 @@ def test_same_length_mask_is_a_window_of_mem_len():
             assert cols[-1] == i + M and np.all(np.diff(cols) == 1)
 
 
+# ------------------------------------------------------ mask variants
+
+def _truncate(d, start):
+    """The same problem with the memory cut to keys start..K-1: keys, values
+    and the r rows of those key positions (row c of r holds distance K-1-c, so
+    the kept rows keep their distances)."""
+    return {**d, "k": d["k"][:, :, start:], "v": d["v"][:, :, start:], "r": d["r"][:, start:]}
+
+
+@pytest.mark.parametrize("M", [0, 3, 6])
+def test_mem_valid_equals_truncated_memory(M):
+    # Per-row memory reset ([XL] "Batched Streams": a reset is per batch row):
+    # a row whose last m memory rows are valid computes exactly the attention
+    # of a memory of length m; m = 0 is the first segment ([SRC] init_mems).
+    L, dh = 5, 8
+    d = synth.relattn_inputs(2, 2, L, M, dh, dtype="f32")
+    full, full_lse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"])
+    for m in range(M + 1):
+        out, lse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], mem_valid=[m, M])
+        t = _truncate(d, M - m)
+        want, want_lse = oracle.relattn_fwd(t["q"][:1], t["k"][:1], t["v"][:1], t["r"], t["u"], t["vb"])
+        np.testing.assert_array_equal(out[:1], want)
+        np.testing.assert_array_equal(lse[:1], want_lse)
+        np.testing.assert_array_equal(out[1], full[1])
+        np.testing.assert_array_equal(lse[1], full_lse[1])
+
+
+@pytest.mark.parametrize("L,M,mem_len", [(6, 4, 4), (6, 4, 2), (5, 7, 3), (4, 3, 9), (7, 2, 5)])
+def test_same_length_rows_are_windows(L, M, mem_len):
+    # same_length ([SRC] MemTransformerLM._forward): every query keeps only the
+    # mem_len key positions ending at itself, i.e. keys j >= i + M + 1 - mem_len.
+    # Rows whose window starts inside the memory equal the plain attention of
+    # that row over the memory cut at the window start (bit-exact); every row
+    # equals scipy's softmax of the plain scores restricted to the window.
+    from scipy.special import softmax
+    dh = 8
+    d = synth.relattn_inputs(1, 2, L, M, dh, dtype="f32")
+    out, lse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], same_length=mem_len)
+    for h in range(2):
+        S = oracle.relattn_scores(d["q"][0, h], d["k"][0, h], d["r"][h], d["u"][h], d["vb"][h], M)
+        for i in range(L):
+            lo = max(0, i + M + 1 - mem_len)
+            s = S[i].copy()
+            s[:lo] = -np.inf
+            np.testing.assert_allclose(out[0, h, i], softmax(s) @ np.asarray(d["v"][0, h], np.float64),
+                                       rtol=1e-12, atol=1e-14)
+            assert abs(lse[0, h, i] - logsumexp(s)) < 1e-12
+            if lo <= M:
+                t = _truncate(d, lo)
+                row, l = oracle.relattn_row(t["q"], t["k"], t["v"], t["r"], t["u"], t["vb"], 0, h, i)
+                np.testing.assert_array_equal(out[0, h, i], row)
+                assert lse[0, h, i] == l
+
+
+def test_same_length_and_mem_valid_combine():
+    # both lower bounds at once: the row sees keys from max(M - m, i + M + 1 - mem_len)
+    L, M, dh, mem_len = 6, 5, 8, 4
+    d = synth.relattn_inputs(2, 1, L, M, dh, dtype="f32")
+    for m in (0, 2, 5):
+        out, _ = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], same_length=mem_len,
+                                    mem_valid=[m, M])
+        for b, mv in ((0, m), (1, M)):
+            for i in range(L):
+                lo = max(M - mv, i + M + 1 - mem_len, 0)
+                if lo <= M:
+                    t = _truncate(d, lo)
+                    row, _ = oracle.relattn_row(t["q"], t["k"], t["v"], t["r"], t["u"], t["vb"], b, 0, i)
+                    np.testing.assert_array_equal(out[b, 0, i], row)
+                row2, _ = oracle.relattn_row(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], b, 0, i,
+                                             same_length=mem_len, mem_valid=mv)
+                np.testing.assert_array_equal(out[b, 0, i], row2)
+
+
 # ------------------------------------------------------------ relative shift
 
 @pytest.mark.parametrize("M", range(0, 9))
