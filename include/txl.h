@@ -81,6 +81,19 @@ typedef struct {
     int64_t v_stride[3];
     int64_t o_stride[3];
     int64_t r_stride[2];
+    /* Optional lower bounds on the visible keys (both off after
+     * txl_relattn_desc_init):
+     *   window > 0: query i sees only keys j >= i + M + 1 - window, the
+     *     `window` positions ending at itself.  With window = mem_len this is
+     *     the same_length mask of [SRC] MemTransformerLM._forward
+     *     (triu(1 + mlen) + tril(-mask_shift_len)).  window < 0 is invalid.
+     *   mem_valid != NULL: DEVICE array [B] of ints; batch row b sees only the
+     *     newest mem_valid[b] memory rows, i.e. keys j >= M - mem_valid[b]
+     *     (a per-row memory reset at a document boundary, [XL] "Batched
+     *     Streams"; the oldest rows hold another document).  Values are
+     *     clamped to [0, M] on the device. */
+    const int *mem_valid;
+    int window;
 } txl_relattn_desc;
 
 /* Fills `desc` for densely packed tensors of the shapes above (splits = 0,
@@ -96,7 +109,8 @@ txl_status txl_relattn_workspace_size(const txl_relattn_desc *desc, size_t *byte
  *
  * For each (b, h) and query i in [0, L), with keys j in [0, K) at positions
  * j - M ([XL] "Batched Tensor Contract"; "Causal Mask With Memory"):
- *   visible(i, j)  <=>  j <= i + M      (all memory, causal current segment)
+ *   visible(i, j)  <=>  lo(b, i) <= j <= i + M   (causal current segment)
+ *   lo(b, i) = max(M - mem_valid[b] (if given), i + M + 1 - window (if > 0), 0)
  *   s_ij = scale * ( (q_i + u) . k_j  +  (q_i + vb) . r_k[L-1-i+j] )
  *   out_i = sum_j softmax_j(s_ij) v_j          over visible j
  *   lse_i = log sum_j exp(s_ij)                over visible j

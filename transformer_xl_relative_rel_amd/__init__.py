@@ -39,7 +39,8 @@ class RelAttnDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("M", ctypes.c_int),
                 ("dh", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("splits", ctypes.c_int),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
-                ("o_stride", ctypes.c_int64 * 3), ("r_stride", ctypes.c_int64 * 2)]
+                ("o_stride", ctypes.c_int64 * 3), ("r_stride", ctypes.c_int64 * 2),
+                ("mem_valid", ctypes.c_void_p), ("window", ctypes.c_int)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -141,12 +142,15 @@ def relattn_workspace_size(q, k, splits: int = 0) -> int:
 
 
 def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, lse=None, want_lse: bool = False,
-                splits: int = 0, workspace=None, stream=None):
+                splits: int = 0, workspace=None, stream=None, window: int = 0, mem_valid=None):
     """Relative attention forward (txl_relattn_fwd).
 
     q [B, H, L, dh]; k, v [B, H, M+L, dh]; r_k [H, M+L, dh] (row c = relative
     position M+L-1-c); u, vb [H, dh] float32.  bf16 or float32 tensors on one
     device; strided views are accepted when the last axis is contiguous.
+    ``window`` > 0 limits query i to keys j >= i + M + 1 - window (same_length);
+    ``mem_valid`` (int32 [B] on the device) keeps only the newest mem_valid[b]
+    memory rows of batch row b.
     Returns out (and lse [B, H, L] float32 when ``want_lse`` or ``lse`` is given).
     """
     import torch
@@ -158,6 +162,11 @@ def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, ls
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("u, vb and lse must be contiguous float32")
     d = _desc(q, k, r_k, out, v, scale, splits)
+    d.window = int(window)
+    if mem_valid is not None:
+        if mem_valid.dtype != torch.int32 or not mem_valid.is_contiguous() or mem_valid.numel() != q.shape[0]:
+            raise ValueError("mem_valid must be a contiguous int32 tensor of B entries")
+        d.mem_valid = mem_valid.data_ptr()
     need = ctypes.c_size_t(0)
     _check(lib().txl_relattn_workspace_size(ctypes.byref(d), ctypes.byref(need)))
     if need.value and workspace is None:

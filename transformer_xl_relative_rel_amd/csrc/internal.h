@@ -25,7 +25,25 @@ struct RelAttnArgs {
     int nsplit;       // key-range splits (1 = normalise in the kernel)
     int tiles_per_split;
     int remap;        // 1: XCD-aware workgroup order (needs B*H % 8 == 0)
+    const int *mem_valid;   // [B] valid memory rows per batch row, or NULL (all M)
+    int window;             // > 0: query i sees keys j >= i + M + 1 - window
 };
+
+// First key visible to query i of batch row b: keys below it are masked.
+__device__ __forceinline__ int key_lo(const RelAttnArgs &a, int b, int i)
+{
+    int lo = 0;
+    if (a.mem_valid) {
+        int mv = a.mem_valid[b];
+        mv = mv < 0 ? 0 : (mv > a.M ? a.M : mv);
+        lo = a.M - mv;
+    }
+    if (a.window > 0) {
+        const int w = i + a.M + 1 - a.window;
+        lo = w > lo ? w : lo;
+    }
+    return lo;
+}
 
 // rb = 16-row blocks per wave (1 or 2).  dtype: 0 = f32, 1 = bf16.
 bool relattn_supported(int dtype, int dh, int rb);

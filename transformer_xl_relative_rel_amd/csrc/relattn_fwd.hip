@@ -233,8 +233,9 @@ struct Kernel {
         const int i0 = qb * BQ;
         const int kv_end = min(i0 + BQ, L) + M;   // keys visible to some row of the block
         const int ntile = (kv_end + BK - 1) / BK;
-        const int kt0 = split * a.tiles_per_split;
-        const int kt1 = min(ntile, kt0 + a.tiles_per_split);
+        // keys below the first query's lower bound are hidden from the whole block
+        const int kt0 = max(split * a.tiles_per_split, key_lo(a, b, i0) / BK);
+        const int kt1 = min(ntile, split * a.tiles_per_split + a.tiles_per_split);
 
         const T *qp = reinterpret_cast<const T *>(a.q) + b * a.qs[0] + h * a.qs[1];
         const T *kp = reinterpret_cast<const T *>(a.k) + b * a.ks[0] + h * a.ks[1];
@@ -300,7 +301,9 @@ struct Kernel {
                 const int blk = wave * RB + rb;
                 const int iq0 = i0 + 16 * blk;
                 if (iq0 >= L) continue;                              // rows past the segment
-                if (j0 > min(iq0 + 15, L - 1) + M) continue;          // tile fully masked
+                const int iql = min(iq0 + 15, L - 1);
+                if (j0 > iql + M) continue;                           // tile fully masked
+                if (j0 + BK - 1 < key_lo(a, b, iq0)) continue;        // below every row's lower bound
                 // ---- position term on the band of r rows: T^T[cc][n] = r[c0 + cc] . (q_n + vb)
                 const int roff = BQ - 16 * (1 + blk);
                 f32x4 t[NBT];
@@ -329,14 +332,17 @@ struct Kernel {
                 for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) sc[tt] = mfma(afrag(sm.ks, 16 * tt + n, kk, g), qu[rb][kk], sc[tt]);
-                // ---- mask: key j visible to query i iff j <= i + M
+                // ---- mask: key j visible to query i iff key_lo(i) <= j <= i + M
                 const int iq = iq0 + n;
-                if (j0 + BK - 1 > iq0 + M) {
+                if (j0 + BK - 1 > iq0 + M || j0 < key_lo(a, b, iql)) {
+                    const int lo = key_lo(a, b, iq);
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (j0 + 16 * tt + 4 * g + v > iq + M) sc[tt][v] = -INFINITY;
+                        for (int v = 0; v < 4; ++v) {
+                            const int j = j0 + 16 * tt + 4 * g + v;
+                            if (j > iq + M || j < lo) sc[tt][v] = -INFINITY;
+                        }
                 }
                 // ---- online softmax in base 2
                 float mx = -INFINITY;

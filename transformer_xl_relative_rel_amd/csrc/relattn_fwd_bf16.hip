@@ -24,7 +24,7 @@
 //   S'^T = K . (c (q + u))^T + T^T      = log2-domain score minus row max;
 //   mask j <= i + M (only on tiles that cross the diagonal), p = exp2(S');
 //   the running max is raised only when a score exceeds it by more than 2^8
-//   (rare branch; the first tile sets it exactly);
+//   (rare branch; a query's first visible tile sets it exactly);
 //   P comes out of the score MFMA in the B-operand layout of
 //   O^T += V^T . P^T  with V^T fragments read from row-major V through the
 //   transposing LDS read; the denominator is one more MFMA against ones.
@@ -146,7 +146,6 @@ struct Tile {
     int kt;      // key tile index (selects the ring quarters)
     int wband;   // first row of this wave's band inside the workgroup band
     int j0, wq0, M;
-    bool first;
 };
 
 // Per-wave state carried across key tiles.
@@ -156,6 +155,7 @@ struct State {
     f32x4 lsum[RB];                     // softmax denominators (all 4 entries equal)
     float mneg[RB];                     // -m: initial accumulator value of the band MFMA
     float mref[RB];                     // running max (log2 units)
+    int klo[RB];                        // first visible key of this lane's query (lower bound)
 };
 
 template <bool MASK>
@@ -248,11 +248,12 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
     auto stage_check = [&](int rb) {
         if constexpr (MASK) {
             const int thr = t.M + t.wq0 + 16 * rb - t.j0;   // visible iff 16 tt + v + d0 <= thr
+            const int thl = st.klo[rb] - t.j0 - 4 * g;      // and 16 tt + v >= thl
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (16 * tt + v + d0 > thr) sc[rb][tt][v] = -INFINITY;
+                    if (16 * tt + v + d0 > thr || 16 * tt + v < thl) sc[rb][tt][v] = -INFINITY;
         }
         float mx = max3(sc[rb][0][0], sc[rb][0][1], sc[rb][0][2]);
         mx = max3(mx, sc[rb][0][3], sc[rb][1][0]);
@@ -262,21 +263,23 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
         mx = max3(mx, sc[rb][2][3], sc[rb][3][0]);
         mx = max3(mx, sc[rb][3][1], sc[rb][3][2]);
         mx = fmaxf(mx, sc[rb][3][3]);
-        if (t.first || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
+        // A query that has not seen a visible key yet (empty denominator) takes
+        // the exact max of its first visible tile; afterwards the max is only
+        // raised when a score exceeds it by more than TAU.
+        const bool fresh = st.lsum[rb][0] == 0.f;
+        if (__builtin_amdgcn_ballot_w64(mx > TAU || (fresh && mx != -INFINITY)) != 0) {
             const float rmx = row_max4(mx);
             float dlt;
-            if (t.first) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the first tile
-            else dlt = fmaxf(rmx, 0.f);                           // only ever raised
+            if (fresh) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the first visible tile
+            else dlt = fmaxf(rmx, 0.f);                         // only ever raised
             st.mref[rb] += dlt;
             st.mneg[rb] -= dlt;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) sc[rb][tt] -= dlt;
-            if (!t.first) {
-                const float alpha = __builtin_amdgcn_exp2f(-dlt);
+            const float alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-dlt);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] *= alpha;
-                st.lsum[rb] *= alpha;
-            }
+            for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] *= alpha;
+            st.lsum[rb] *= alpha;
         }
     };
     // probabilities as bf16 B fragments
@@ -346,8 +349,9 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
     const int i0 = qb * BQ;
     const int kv_end = min(i0 + BQ, L) + M;
     const int ntile = (kv_end + BK - 1) / BK;
-    const int kt0 = split * a.tiles_per_split;
-    const int kt1 = min(ntile, kt0 + a.tiles_per_split);
+    // keys below the first query's lower bound are hidden from the whole block
+    const int kt0 = max(split * a.tiles_per_split, key_lo(a, b, i0) / BK);
+    const int kt1 = min(ntile, split * a.tiles_per_split + a.tiles_per_split);
 
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1];
     const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
@@ -390,7 +394,10 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
         st.lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.mneg[rb] = 0.f;
         st.mref[rb] = 0.f;
+        st.klo[rb] = key_lo(a, b, iqc);
     }
+    const int wlo_first = key_lo(a, b, wq0);                      // smallest lower bound of the wave
+    const int wlo_last = key_lo(a, b, min(wq0 + 16 * RB - 1, L - 1));   // largest
 
     // ---- direct loads: thread tid moves chunk tid of each tile (row tid / 8),
     // reading the chunk the XOR swizzle puts at that LDS position.  Rows outside
@@ -432,7 +439,7 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
             load_kv(kt + 1);
             load_r_quarter(kt + NQ - 1);
         }
-        if (wq0 < L && j0 <= min(wq0 + 16 * RB - 1, L - 1) + M) {
+        if (wq0 < L && j0 <= min(wq0 + 16 * RB - 1, L - 1) + M && j0 + BK - 1 >= wlo_first) {
             Tile t;
             t.sk = sk[kt & 1];
             t.sv = sv[kt & 1];
@@ -443,8 +450,7 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
             t.j0 = j0;
             t.wq0 = wq0;
             t.M = M;
-            t.first = (kt == kt0);
-            if (j0 + BK - 1 > wq0 + M) tile_body<true>(st, t, g, n);
+            if (j0 + BK - 1 > wq0 + M || j0 < wlo_last) tile_body<true>(st, t, g, n);
             else tile_body<false>(st, t, g, n);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed

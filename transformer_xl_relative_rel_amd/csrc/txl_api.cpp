@@ -111,6 +111,9 @@ txl_status check_desc(const txl_relattn_desc *d)
         return fail(TXL_ERR_UNSUPPORTED, "dh=%d is not supported for dtype %s (bf16: 32/64/128, f32: 16/32/64)", d->dh,
                     d->dtype == TXL_BF16 ? "bf16" : "f32");
     if (!std::isfinite(d->scale)) return fail(TXL_ERR_INVALID_ARG, "scale is not finite");
+    if (d->window < 0) return fail(TXL_ERR_INVALID_ARG, "window must be >= 0 (got %d)", d->window);
+    if (d->mem_valid && (reinterpret_cast<uintptr_t>(d->mem_valid) & 3u))
+        return fail(TXL_ERR_INVALID_ARG, "mem_valid must be 4-byte aligned");
     const size_t es = elem_size(d->dtype);
     const int64_t *strides[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
     const char *names[4] = {"q", "k", "v", "out"};
@@ -242,6 +245,8 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     a.nsplit = p.nsplit;
     a.tiles_per_split = p.tps;
     a.remap = ((d->B * d->H) % 8 == 0) ? 1 : 0;
+    a.mem_valid = d->mem_valid;
+    a.window = d->window;
     hipError_t e = p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
                           : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn launch failed: %s", hipGetErrorString(e));
