@@ -70,10 +70,12 @@ def _load():
         lib.txo_linear.argtypes = [_I, _I, _I, _D, _D, _D, _D]
         lib.txo_layer_norm.argtypes = [_I, _I, _D, _D, _D, ctypes.c_double, _D]
         lib.txo_layer_fwd.argtypes = [_I] * 7 + [_D] * 15 + [ctypes.c_double, _D]
+        lib.txo_layer_fwd_ex.argtypes = [_I] * 9 + [ctypes.POINTER(_I)] + [_D] * 15 + [ctypes.c_double, _D]
         for name in ("txo_visible_mask", "txo_visible_mask_same_length", "txo_rel_shift",
                      "txo_relattn_scores", "txo_relattn_fwd_range", "txo_relattn_row",
                      "txo_relattn_fwd_vis_range", "txo_relattn_row_vis",
-                     "txo_mem_update", "txo_pos_emb", "txo_linear", "txo_layer_norm", "txo_layer_fwd"):
+                     "txo_mem_update", "txo_pos_emb", "txo_linear", "txo_layer_norm", "txo_layer_fwd",
+                     "txo_layer_fwd_ex"):
             getattr(lib, name).restype = _I
         _lib = lib
         return lib
@@ -253,8 +255,11 @@ def layer_norm(x, g, b, eps: float = 1e-5) -> np.ndarray:
 LAYER_KEYS = ("W_qkv", "W_r", "W_o", "ln1_g", "ln1_b", "W1", "b1", "W2", "b2", "ln2_g", "ln2_b")
 
 
-def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, eps: float = 1e-5) -> np.ndarray:
-    """One post-LN decoder layer (see txo_layer_fwd).  h_in [B, L, d]; mem [B, M_cur, d] or None."""
+def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, eps: float = 1e-5, clamp_len: int = 0,
+              same_length: int = 0, mem_valid=None) -> np.ndarray:
+    """One post-LN decoder layer (see txo_layer_fwd_ex).  h_in [B, L, d]; mem [B, M_cur, d] or None.
+    clamp_len / same_length as in [SRC] MemTransformerLM (0 = off); mem_valid [B] ints in
+    [0, M_cur] keeps only the newest mem_valid[b] memory rows of row b."""
     h_in = _f64(h_in)
     B, L, d = h_in.shape
     M_cur = 0 if mem is None else mem.shape[1]
@@ -262,8 +267,14 @@ def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, eps: float = 
     ws = [_f64(w[key]) for key in LAYER_KEYS]
     d_inner = ws[5].shape[0]
     out = np.empty_like(h_in)
-    _check(_load().txo_layer_fwd(B, L, M_cur, d, n_head, d_head, d_inner, _p(h_in), _p(memd),
-                                 *[_p(a) for a in ws], _p(_f64(u)), _p(_f64(vb)), eps, _p(out)),
+    mv = None
+    if mem_valid is not None:
+        mv = np.ascontiguousarray(np.asarray(mem_valid, dtype=np.int32))
+        assert mv.shape == (B,)
+    mvp = mv.ctypes.data_as(ctypes.POINTER(_I)) if mv is not None else None
+    _check(_load().txo_layer_fwd_ex(B, L, M_cur, d, n_head, d_head, d_inner, int(clamp_len), int(same_length), mvp,
+                                    _p(h_in), _p(memd), *[_p(a) for a in ws], _p(_f64(u)), _p(_f64(vb)), eps,
+                                    _p(out)),
            "layer_fwd")
     return out
 

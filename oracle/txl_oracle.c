@@ -517,16 +517,26 @@ int txo_layer_norm(int N, int d, const double *x, const double *g, const double 
  * mem + b*M_cur*d (M_cur may be 0 and mem NULL), out [L][d].
  * W_qkv [3*H*dh][d], W_r [H*dh][d], W_o [d][H*dh], W1 [d_inner][d], b1
  * [d_inner], W2 [d][d_inner], b2 [d]; u, vb [H][dh]. */
-int txo_layer_fwd(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
-                  const double *h_in, const double *mem,
-                  const double *W_qkv, const double *W_r, const double *W_o,
-                  const double *ln1_g, const double *ln1_b,
-                  const double *W1, const double *b1, const double *W2, const double *b2,
-                  const double *ln2_g, const double *ln2_b,
-                  const double *u, const double *vb, double eps, double *out)
+/* The layer with the options of [SRC] MemTransformerLM: clamp_len > 0 clamps
+ * the position values ([SRC] _forward: pos_seq.clamp_(max=clamp_len)),
+ * same_len > 0 selects the same_length mask with mem_len = same_len, and
+ * mem_valid ([B] or NULL) hides the oldest M_cur - mem_valid[b] memory rows of
+ * batch row b (per-row memory reset, see head_visible). */
+int txo_layer_fwd_ex(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
+                     int clamp_len, int same_len, const int *mem_valid,
+                     const double *h_in, const double *mem,
+                     const double *W_qkv, const double *W_r, const double *W_o,
+                     const double *ln1_g, const double *ln1_b,
+                     const double *W1, const double *b1, const double *W2, const double *b2,
+                     const double *ln2_g, const double *ln2_b,
+                     const double *u, const double *vb, double eps, double *out)
 {
     if (B < 1 || L < 1 || M_cur < 0 || d < 2 || (d & 1) || H < 1 || dh < 1 || d_inner < 1) return TXO_EINVAL;
     if (M_cur > 0 && !mem) return TXO_EINVAL;
+    if (clamp_len < 0 || same_len < 0) return TXO_EINVAL;
+    if (mem_valid)
+        for (int b = 0; b < B; ++b)
+            if (mem_valid[b] < 0 || mem_valid[b] > M_cur) return TXO_EINVAL;
     int K = M_cur + L, HD = H * dh;
     double scale = 1.0 / sqrt((double)dh);
     double *cat = malloc((size_t)K * d * sizeof(double));
@@ -544,14 +554,18 @@ int txo_layer_fwd(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
     double *x = malloc((size_t)L * d * sizeof(double));
     double *f1 = malloc((size_t)L * d_inner * sizeof(double));
     double *f2 = malloc((size_t)L * d * sizeof(double));
+    unsigned char *vis = malloc((size_t)L * K);
     int rc = TXO_OK;
-    if (!cat || !heads || !pe || !rk || !qh || !kh || !vh || !rh || !S || !oh || !vec || !ao || !x || !f1 || !f2) {
+    if (!cat || !heads || !pe || !rk || !qh || !kh || !vh || !rh || !S || !oh || !vec || !ao || !x || !f1 || !f2 ||
+        !vis) {
         rc = TXO_ENOMEM;
         goto done;
     }
-    txo_pos_emb(K, d, 0, pe);
+    txo_pos_emb(K, d, clamp_len, pe);
     linear(K, d, HD, pe, W_r, NULL, rk);                 /* r_head_k [K][H][dh] */
     for (int b = 0; b < B; ++b) {
+        rc = head_visible(L, M_cur, same_len, mem_valid ? mem_valid[b] : M_cur, vis);
+        if (rc != TXO_OK) goto done;
         const double *hb = h_in + (size_t)b * L * d;
         for (int t = 0; t < M_cur; ++t)
             for (int i = 0; i < d; ++i) cat[(size_t)t * d + i] = mem[((size_t)b * M_cur + t) * d + i];
@@ -568,7 +582,7 @@ int txo_layer_fwd(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
                     vh[(size_t)t * dh + e] = heads[(size_t)t * 3 * HD + 2 * HD + n * dh + e];
                     rh[(size_t)t * dh + e] = rk[(size_t)t * HD + n * dh + e];
                 }
-            head_scores_direct(L, M_cur, dh, scale, qh, kh, rh, u + (size_t)n * dh, vb + (size_t)n * dh, S);
+            head_scores_vis(L, M_cur, dh, scale, qh, kh, rh, u + (size_t)n * dh, vb + (size_t)n * dh, vis, S);
             head_softmax_pv(L, K, dh, S, vh, oh, NULL);
             for (int t = 0; t < L; ++t)
                 for (int e = 0; e < dh; ++e) vec[(size_t)t * HD + n * dh + e] = oh[(size_t)t * dh + e];
@@ -584,6 +598,19 @@ int txo_layer_fwd(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
     }
 done:
     free(cat); free(heads); free(pe); free(rk); free(qh); free(kh); free(vh); free(rh);
-    free(S); free(oh); free(vec); free(ao); free(x); free(f1); free(f2);
+    free(S); free(oh); free(vec); free(ao); free(x); free(f1); free(f2); free(vis);
     return rc;
+}
+
+/* [SRC] RelPartialLearnableDecoderLayer with the default options. */
+int txo_layer_fwd(int B, int L, int M_cur, int d, int H, int dh, int d_inner,
+                  const double *h_in, const double *mem,
+                  const double *W_qkv, const double *W_r, const double *W_o,
+                  const double *ln1_g, const double *ln1_b,
+                  const double *W1, const double *b1, const double *W2, const double *b2,
+                  const double *ln2_g, const double *ln2_b,
+                  const double *u, const double *vb, double eps, double *out)
+{
+    return txo_layer_fwd_ex(B, L, M_cur, d, H, dh, d_inner, 0, 0, NULL, h_in, mem, W_qkv, W_r, W_o, ln1_g, ln1_b,
+                            W1, b1, W2, b2, ln2_g, ln2_b, u, vb, eps, out);
 }

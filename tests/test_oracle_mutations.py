@@ -34,6 +34,7 @@ MUTATIONS = [
     ("mem_valid_off_by_one", "for (int j = 0; j < M - mvalid; ++j) vis",
      "for (int j = 0; j < M - mvalid + 1 && j < K; ++j) vis"),
     ("same_length_shift", "int lower = (j - i) <= -shift;", "int lower = (j - i) < -shift;"),
+    ("layer_ignores_clamp", "txo_pos_emb(K, d, clamp_len, pe);", "txo_pos_emb(K, d, 0, pe);"),
 ]
 
 PINS = [
@@ -49,6 +50,7 @@ PINS = [
     pins.test_m0_zero_position_is_causal_sdpa,
     lambda: pins.test_mem_valid_equals_truncated_memory(3),
     lambda: pins.test_same_length_rows_are_windows(6, 4, 4),
+    lambda: pins.test_layer_options_match_torch_third_opinion(3, 0, None),
 ]
 
 

@@ -425,10 +425,12 @@ def random_layer(d, H, dh, d_inner, rng, scale=0.3):
     }
 
 
-def torch_layer(h, mem, w, u, vb, H, dh, eps=1e-5):
+def torch_layer(h, mem, w, u, vb, H, dh, eps=1e-5, clamp_len=0, window=0, mem_valid=None):
     """Third opinion, torch fp64 library routines on the CPU: projections with
     F.linear, the position term gathered through the golden distance ids,
-    attention with scaled_dot_product_attention, then the post-LN blocks."""
+    attention with scaled_dot_product_attention, then the post-LN blocks.
+    Options: clamp_len (position values clamped), window (query i keeps keys
+    j >= i + M + 1 - window) and mem_valid (row b keeps keys j >= M - mem_valid[b])."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
     h, w = t(h), {key: t(val) for key, val in w.items()}
     B, L, d = h.shape
@@ -440,10 +442,17 @@ def torch_layer(h, mem, w, u, vb, H, dh, eps=1e-5):
     q = heads[:, -L:, :HD].reshape(B, L, H, dh).permute(0, 2, 1, 3)
     k = heads[:, :, HD:2 * HD].reshape(B, K, H, dh).permute(0, 2, 1, 3)
     v = heads[:, :, 2 * HD:].reshape(B, K, H, dh).permute(0, 2, 1, 3)
-    pe = t(oracle.pos_emb(K, d))  # pinned separately by its closed forms
+    pe = t(oracle.pos_emb(K, d, clamp_len))  # pinned separately by its closed forms
     r = F.linear(pe, w["W_r"]).reshape(K, H, dh).permute(1, 0, 2)   # [H, K, dh]
     ids = torch.from_numpy(reference_rel_ids(L, M))
-    vis = torch.from_numpy(make_txl_mask(L, M))
+    vis = torch.from_numpy(make_txl_mask(L, M))[None].repeat(B, 1, 1)
+    jj = torch.arange(K)[None, :]
+    if window:
+        vis &= jj >= torch.arange(L)[:, None] + M + 1 - window
+    if mem_valid is not None:
+        for b in range(B):
+            vis[b] &= jj >= M - mem_valid[b]
+    vis = vis[:, None]                                               # [B, 1, L, K]
     rg = r[:, (K - 1 - ids).clamp(0, K - 1)]                         # [H, L, K, dh]
     bias = torch.einsum("bhid,hijd->bhij", q + t(vb)[None, :, None], rg) / math.sqrt(dh)
     am = torch.where(vis, bias, torch.tensor(-math.inf, dtype=torch.float64))
@@ -469,6 +478,36 @@ def test_layer_matches_torch_third_opinion(M_cur):
     y = oracle.layer_fwd(h, mem, w2, u, vb, H, dh, eps=0.0)
     np.testing.assert_allclose(y.mean(-1), 0.0, atol=1e-12)
     np.testing.assert_allclose(y.var(-1), 1.0, atol=1e-10)
+
+
+@pytest.mark.parametrize("clamp_len,window,mem_valid", [(3, 0, None), (0, 4, None), (0, 0, [0, 3]),
+                                                        (2, 7, [5, 1])])
+def test_layer_options_match_torch_third_opinion(clamp_len, window, mem_valid):
+    # clamp_len, same_length (the oracle builds the page's triu + tril mask,
+    # torch the window j >= i + M + 1 - mem_len) and per-row memory validity
+    rng = _rng(60 + clamp_len + window)
+    B, L, d, H, dh, di, M_cur = 2, 6, 8, 2, 4, 12, 5
+    w = random_layer(d, H, dh, di, rng)
+    u, vb = rng.standard_normal((H, dh)), rng.standard_normal((H, dh))
+    h = rng.standard_normal((B, L, d))
+    mem = rng.standard_normal((B, M_cur, d))
+    got = oracle.layer_fwd(h, mem, w, u, vb, H, dh, clamp_len=clamp_len, same_length=window, mem_valid=mem_valid)
+    want = torch_layer(h, mem, w, u, vb, H, dh, clamp_len=clamp_len, window=window, mem_valid=mem_valid)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+
+
+def test_layer_mem_valid_equals_truncated_memory():
+    # a row with m valid memory rows computes the layer on a memory of m rows (bit-exact)
+    rng = _rng(70)
+    B, L, d, H, dh, di, M_cur = 1, 5, 8, 2, 4, 12, 6
+    w = random_layer(d, H, dh, di, rng)
+    u, vb = rng.standard_normal((H, dh)), rng.standard_normal((H, dh))
+    h = rng.standard_normal((B, L, d))
+    mem = rng.standard_normal((B, M_cur, d))
+    for m in range(M_cur + 1):
+        got = oracle.layer_fwd(h, mem, w, u, vb, H, dh, mem_valid=[m])
+        want = oracle.layer_fwd(h, mem[:, M_cur - m:] if m else None, w, u, vb, H, dh)
+        np.testing.assert_array_equal(got, want)
 
 
 def test_stack_memory_holds_earlier_hidden_states():
