@@ -144,7 +144,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(os.path.join(ROOT, "transformer_xl_relative_rel_amd", "csrc",
                                                               "relattn_fwd_bf16.hip")),
-                     "kernel": "relattn_fwd_bf16_kernel<64>", "kernel_ms": round(attn_ms, 5)},
+                     "kernel": "relattn_fwd_bf16_kernel", "kernel_ms": round(attn_ms, 5)},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(d, B, H, L, M, dh)

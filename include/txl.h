@@ -184,6 +184,17 @@ txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, 
 typedef struct {
     int B, L, d_model, n_head, d_head, d_inner;
     float ln_eps;      /* <= 0 selects 1e-5 */
+    /* Options of [SRC] MemTransformerLM (all 0 / NULL = off):
+     *   clamp_len > 0: position values above clamp_len use the encoding of
+     *     clamp_len ([SRC] _forward: pos_seq.clamp_(max=clamp_len));
+     *   same_length > 0: the same_length mask with mem_len = same_length, i.e.
+     *     query i sees keys j >= i + M_cur + 1 - same_length (txl_relattn_desc
+     *     window);
+     *   mem_valid: DEVICE [B] ints, row b keeps only its newest mem_valid[b]
+     *     memory rows (per-row reset, txl_relattn_desc mem_valid). */
+    int clamp_len;
+    int same_length;
+    const int *mem_valid;
 } txl_layer_desc;
 
 typedef struct {

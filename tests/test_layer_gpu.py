@@ -140,3 +140,65 @@ def test_stack_segments_against_oracle():
             want = oracle.mem_update(old, hids[n].view(torch.int16).cpu().numpy(), mem_len)
             assert np.array_equal(new[n].view(torch.int16).cpu().numpy(), want)
         mems = new
+
+
+@pytest.mark.parametrize("clamp_len,same_length,mem_valid", [(5, 0, None), (0, 20, None), (0, 0, [0, 9]),
+                                                             (7, 24, [16, 3])])
+def test_layer_options_match_oracle(clamp_len, same_length, mem_valid):
+    """clamp_len, same_length and per-row memory validity against the oracle layer."""
+    B, L, M_cur, d, H, dh, di = 2, 24, 16, 128, 2, 64, 256
+    log(f"case: layer options clamp{clamp_len} same_length{same_length} mem_valid{mem_valid}")
+    w = make_layer(d, H, dh, di, 31)
+    h = rnd((B, L, d), 32, 1.0).astype(np.float64)
+    mem = rnd((B, M_cur, d), 33, 1.0).astype(np.float64)
+    u = synth.normal((H, dh), 34, 0.5)
+    vb = synth.normal((H, dh), 35, 0.5)
+    want = oracle.layer_fwd(h, mem, w, u, vb, H, dh, clamp_len=clamp_len, same_length=same_length,
+                            mem_valid=mem_valid)
+    tu = torch.from_numpy(np.asarray(u, np.float32)).to(DEV)
+    tv = torch.from_numpy(np.asarray(vb, np.float32)).to(DEV)
+    mv = None if mem_valid is None else torch.tensor(mem_valid, dtype=torch.int32, device=DEV)
+    got = txl.layer_fwd(bf(h), bf(mem), to_dev(w), tu, tv, H, dh, clamp_len=clamp_len, same_length=same_length,
+                        mem_valid=mv)
+    torch.cuda.synchronize()
+    check(got.float().cpu().numpy(), want, "layer out")
+
+
+def test_stack_with_per_row_resets():
+    """Two layers over four segments of three streams; rows 0 and 2 start new
+    documents at segments 2 and 1.  The device keeps full memory buffers and a
+    per-row count of valid memory rows; every layer output of every row must
+    equal the oracle layer run on that row alone with only its valid memory
+    ([XL] "Batched Streams": memory belongs to the row's own stream)."""
+    log("case: 2-layer stack, 4 segments, per-row resets")
+    B, L, d, H, dh, di, mem_len, n_layer = 3, 16, 128, 2, 64, 256, 24, 2
+    resets = {1: [2], 2: [0]}
+    layers = [make_layer(d, H, dh, di, 500 * (n + 1)) for n in range(n_layer)]
+    dlayers = [to_dev(w) for w in layers]
+    u = synth.normal((H, dh), 41, 0.5)
+    vb = synth.normal((H, dh), 42, 0.5)
+    tu = torch.from_numpy(np.asarray(u, np.float32)).to(DEV)
+    tv = torch.from_numpy(np.asarray(vb, np.float32)).to(DEV)
+    mems = [None] * (n_layer + 1)
+    valid = [0] * B
+    for seg in range(4):
+        for b in resets.get(seg, []):
+            valid[b] = 0
+        M_cur = 0 if mems[0] is None else mems[0].shape[1]
+        mv = torch.tensor([min(v, M_cur) for v in valid], dtype=torch.int32, device=DEV)
+        x = bf(rnd((B, L, d), 600 + seg, 1.0))
+        hids = [x]
+        for n in range(n_layer):
+            hids.append(txl.layer_fwd(hids[n], mems[n], dlayers[n], tu, tv, H, dh,
+                                      mem_valid=mv if M_cur else None))
+        torch.cuda.synchronize()
+        for n in range(n_layer):
+            hin = hids[n].float().cpu().numpy().astype(np.float64)
+            for b in range(B):
+                m = min(valid[b], M_cur)
+                mem_b = None if m == 0 else mems[n][b:b + 1, M_cur - m:].float().cpu().numpy().astype(np.float64)
+                want = oracle.layer_fwd(hin[b:b + 1], mem_b, layers[n], u, vb, H, dh)
+                check(hids[n + 1][b:b + 1].float().cpu().numpy(), want, f"segment {seg} layer {n} row {b}")
+        mems = txl.mem_update_batched(mems if mems[0] is not None else None, hids, mem_len)
+        torch.cuda.synchronize()
+        valid = [min(mems[0].shape[1], v + L) for v in valid]

@@ -45,7 +45,8 @@ class RelAttnDesc(ctypes.Structure):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("L", ctypes.c_int), ("d_model", ctypes.c_int), ("n_head", ctypes.c_int),
-                ("d_head", ctypes.c_int), ("d_inner", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+                ("d_head", ctypes.c_int), ("d_inner", ctypes.c_int), ("ln_eps", ctypes.c_float),
+                ("clamp_len", ctypes.c_int), ("same_length", ctypes.c_int), ("mem_valid", ctypes.c_void_p)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -223,7 +224,7 @@ def mem_update_batched(mems, hs, mem_len: int, ext_len: int = 0, outs=None, stre
 
 def _layer_desc(h_in, w, n_head: int, d_head: int, eps: float) -> LayerDesc:
     B, L, d = h_in.shape
-    return LayerDesc(B, L, d, n_head, d_head, w["W1"].shape[0], eps)
+    return LayerDesc(B, L, d, n_head, d_head, w["W1"].shape[0], eps, 0, 0, None)
 
 
 def layer_workspace_size(h_in, w, n_head: int, d_head: int, M_cur: int, eps: float = 1e-5) -> int:
@@ -235,16 +236,24 @@ def layer_workspace_size(h_in, w, n_head: int, d_head: int, M_cur: int, eps: flo
 
 
 def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, *, eps: float = 1e-5, out=None, workspace=None,
-              stream=None):
+              stream=None, clamp_len: int = 0, same_length: int = 0, mem_valid=None):
     """One post-LN decoder layer (txl_layer_fwd).
 
     h_in [B, L, d] bf16; mem [B, M_cur, d] bf16 or None; w maps LAYER_KEYS to
     tensors (matrices bf16 in nn.Linear [out, in] layout, vectors float32, b1 /
-    b2 may be None); u, vb [H, dh] float32.  Returns h_out [B, L, d] bf16.
+    b2 may be None); u, vb [H, dh] float32.  clamp_len / same_length as in
+    [SRC] MemTransformerLM (0 = off); mem_valid: int32 [B] on the device.
+    Returns h_out [B, L, d] bf16.
     """
     import torch
     M_cur = 0 if mem is None else mem.shape[1]
     desc = _layer_desc(h_in, w, n_head, d_head, eps)
+    desc.clamp_len = int(clamp_len)
+    desc.same_length = int(same_length)
+    if mem_valid is not None:
+        if mem_valid.dtype != torch.int32 or not mem_valid.is_contiguous() or mem_valid.numel() != h_in.shape[0]:
+            raise ValueError("mem_valid must be a contiguous int32 tensor of B entries")
+        desc.mem_valid = mem_valid.data_ptr()
     if out is None:
         out = torch.empty_like(h_in)
     for t in [h_in, out] + ([mem] if M_cur else []) + [w[k] for k in LAYER_KEYS if w.get(k) is not None]:

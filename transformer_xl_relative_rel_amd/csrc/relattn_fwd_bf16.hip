@@ -141,6 +141,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 struct Tile {
+    bool first;  // first tile of this key range
     const u32x4 *sk, *sv, *sr;
     float *skw;
     int kt;      // key tile index (selects the ring quarters)
@@ -158,7 +159,9 @@ struct State {
     int klo[RB];                        // first visible key of this lane's query (lower bound)
 };
 
-template <bool MASK>
+// LOWER: some query has a lower key bound (window or memory validity), so a
+// query's first visible tile need not be the first tile of the range.
+template <bool MASK, bool LOWER>
 __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n)
 {
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
@@ -248,12 +251,12 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
     auto stage_check = [&](int rb) {
         if constexpr (MASK) {
             const int thr = t.M + t.wq0 + 16 * rb - t.j0;   // visible iff 16 tt + v + d0 <= thr
-            const int thl = st.klo[rb] - t.j0 - 4 * g;      // and 16 tt + v >= thl
+            const int thl = LOWER ? st.klo[rb] - t.j0 - 4 * g : 0;   // and 16 tt + v >= thl
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (16 * tt + v + d0 > thr || 16 * tt + v < thl) sc[rb][tt][v] = -INFINITY;
+                    if (16 * tt + v + d0 > thr || (LOWER && 16 * tt + v < thl)) sc[rb][tt][v] = -INFINITY;
         }
         float mx = max3(sc[rb][0][0], sc[rb][0][1], sc[rb][0][2]);
         mx = max3(mx, sc[rb][0][3], sc[rb][1][0]);
@@ -263,11 +266,14 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
         mx = max3(mx, sc[rb][2][3], sc[rb][3][0]);
         mx = max3(mx, sc[rb][3][1], sc[rb][3][2]);
         mx = fmaxf(mx, sc[rb][3][3]);
-        // A query that has not seen a visible key yet (empty denominator) takes
-        // the exact max of its first visible tile; afterwards the max is only
-        // raised when a score exceeds it by more than TAU.
-        const bool fresh = st.lsum[rb][0] == 0.f;
-        if (__builtin_amdgcn_ballot_w64(mx > TAU || (fresh && mx != -INFINITY)) != 0) {
+        // A query that has not seen a visible key yet takes the exact max of its
+        // first visible tile; afterwards the max is only raised when a score
+        // exceeds it by more than TAU.  Without lower key bounds that tile is
+        // the first tile of the range; with them, a query is fresh while its
+        // denominator is still empty.
+        const bool fresh = LOWER ? st.lsum[rb][0] == 0.f : t.first;
+        if ((!LOWER && t.first) ||
+            __builtin_amdgcn_ballot_w64(mx > TAU || (LOWER && fresh && mx != -INFINITY)) != 0) {
             const float rmx = row_max4(mx);
             float dlt;
             if (fresh) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the first visible tile
@@ -322,6 +328,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
     }
 }
 
+template <bool LOWER>
 __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 {
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
@@ -450,8 +457,9 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
             t.j0 = j0;
             t.wq0 = wq0;
             t.M = M;
-            if (j0 + BK - 1 > wq0 + M || j0 < wlo_last) tile_body<true>(st, t, g, n);
-            else tile_body<false>(st, t, g, n);
+            t.first = (kt == kt0);
+            if (j0 + BK - 1 > wq0 + M || j0 < wlo_last) tile_body<true, LOWER>(st, t, g, n);
+            else tile_body<false, LOWER>(st, t, g, n);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
@@ -495,7 +503,10 @@ hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s)
 {
     if (dh != DH) return hipErrorInvalidValue;
     const int blocks = a.nqb * a.B * a.H * a.nsplit;
-    hipLaunchKernelGGL(relattn_fwd_bf16_kernel, dim3(blocks), dim3(NW * 64), 0, s, a);
+    if (a.window > 0 || a.mem_valid)
+        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<true>, dim3(blocks), dim3(NW * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<false>, dim3(blocks), dim3(NW * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_relattn_combine(a, 1, dh, s);

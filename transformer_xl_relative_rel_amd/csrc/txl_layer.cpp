@@ -109,6 +109,8 @@ void attn_desc(const txl_layer_desc &d, int M_cur, txl_relattn_desc &a)
     std::memcpy(a.v_stride, a.q_stride, sizeof a.q_stride);
     a.o_stride[0] = (int64_t)d.L * HD; a.o_stride[1] = d.d_head; a.o_stride[2] = HD;
     a.r_stride[0] = d.d_head; a.r_stride[1] = HD;
+    a.window = d.same_length;
+    a.mem_valid = d.mem_valid;
 }
 
 txl_status check_layer(const txl_layer_desc *d, int M_cur)
@@ -121,6 +123,8 @@ txl_status check_layer(const txl_layer_desc *d, int M_cur)
         return fail(TXL_ERR_INVALID_ARG, "d_model, n_head*d_head and d_inner must be multiples of 8");
     if (d->d_model > txl::layer_norm_max_width())
         return fail(TXL_ERR_UNSUPPORTED, "d_model=%d exceeds %d", d->d_model, txl::layer_norm_max_width());
+    if (d->clamp_len < 0 || d->same_length < 0)
+        return fail(TXL_ERR_INVALID_ARG, "clamp_len and same_length must be >= 0");
     if (d->d_head != 32 && d->d_head != 64 && d->d_head != 128)
         return fail(TXL_ERR_UNSUPPORTED, "d_head=%d (bf16 attention supports 32, 64, 128)", d->d_head);
     const int64_t K = (int64_t)M_cur + d->L;
@@ -225,7 +229,7 @@ txl_status txl_layer_fwd(const txl_layer_desc *d, const txl_layer_weights *w, co
     if ((bs = (call)) != rocblas_status_success) return fail(TXL_ERR_HIP, "%s failed: %s", #call, rocblas_status_to_string(bs))
 
     // r_k = pos W_r^T  [K][HD]
-    TXL_HIP(txl::launch_pos_emb(pe, K, D, 0, st));
+    TXL_HIP(txl::launch_pos_emb(pe, K, D, d->clamp_len, st));
     TXL_BLAS(gemm_xwt(bh, HD, K, D, w->W_r, D, pe, D, 0, rk, rocblas_datatype_bf16_r, HD, 0, 1));
     // [q; k; v] of the current rows, [k; v] of the memory rows, into qkv[b][row][3 HD]
     TXL_BLAS(gemm_xwt(bh, 3 * HD, L, D, Wqkv, D, h_in, D, (int64_t)L * D, qkv + (size_t)M_cur * 3 * HD,
