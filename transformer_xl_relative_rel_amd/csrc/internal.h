@@ -49,8 +49,9 @@ __device__ __forceinline__ int key_lo(const RelAttnArgs &a, int b, int i)
 bool relattn_supported(int dtype, int dh, int rb);
 hipError_t launch_relattn(const RelAttnArgs &a, int dtype, int dh, int rb, hipStream_t s);
 
-// bf16 throughput kernel (dh = 64): query rows per workgroup, and launch.
-int relattn_bf16_rows_per_block();
+// bf16 throughput kernel (dh = 64): workgroups per (b, h) along the queries
+// (before key splits), and launch.
+int relattn_bf16_groups_per_head(int L);
 bool relattn_bf16_supported(int dh);
 hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s);
 // Key-range combine used by both kernels when nsplit > 1.

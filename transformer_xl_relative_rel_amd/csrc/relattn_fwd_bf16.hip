@@ -8,38 +8,45 @@
 //   s_ij = scale * ((q_i + u) . k_j + (q_i + vb) . r[L-1-i+j]),
 //   visible iff j <= i + M,  out_i = softmax_j(s_ij) . v_j.
 //
-// Work decomposition.  A workgroup is 8 waves (two per SIMD) and owns 256
-// query rows of one (b, h); each wave owns 32 rows as two 16-query blocks.
-// Keys are walked in tiles of 64.  Waves w and w + 4 share a SIMD and own
-// 32-query blocks s and 7 - s, whose key ranges add up to the same length.
+// Work decomposition.  The queries of one (b, h) are cut into runs of 32
+// (two 16-query blocks each) and the runs are paired from both ends: pair p
+// is runs p and nr-1-p, so every pair covers the same number of (query, key)
+// tiles.  A workgroup owns four pairs and is 8 waves: waves w and w + 4 share
+// a SIMD and take the two runs of pair w, so every SIMD and every workgroup
+// carries the same work.  A wave keeps its two blocks' state in registers and
+// reads each K and V fragment from LDS once per key tile for both blocks.
+// Keys are walked in tiles of 64.
 //
 // Everything is computed transposed (keys on MFMA rows, queries on lanes):
 //   T^T = R_band . (c (q + vb))^T - m   with c = scale * log2(e) folded into
 //       the query operand and the running row max m of each query folded into
 //       the accumulator's initial value; 16 queries need 79 consecutive r rows
-//       per 64-key tile: 5 band MFMA tiles;
-//   the band value of (query n, r row cc) belongs to key jj = cc + n - 15: it
+//       per 64-key tile: 5 band MFMA tiles.  Along a band row the key minus the
+//       query is fixed, so the causal bound j <= i + M (and the same_length
+//       window) is a threshold on the band row shared by the whole block: on
+//       the few tiles that need it, masked band rows start at -inf.
+//   the band value of (query n, band row cc) belongs to key jj = cc + n - 15: it
 //   is written to a per-wave LDS row at column cc + n + 1 and read back in key
 //   order as the initial accumulator of
 //   S'^T = K . (c (q + u))^T + T^T      = log2-domain score minus row max;
-//   mask j <= i + M (only on tiles that cross the diagonal), p = exp2(S');
-//   the running max is raised only when a score exceeds it by more than 2^8
-//   (rare branch; a query's first visible tile sets it exactly);
+//   p = exp2(S'); the running max is raised only when a score exceeds it by
+//   more than 2^8 (rare branch; a query's first visible tile sets it exactly);
 //   P comes out of the score MFMA in the B-operand layout of
 //   O^T += V^T . P^T  with V^T fragments read from row-major V through the
 //   transposing LDS read; the denominator is one more MFMA against ones.
-// The two blocks of a wave are software-pipelined: the softmax of block 0
-// sits in one basic block with the band and content MFMAs of block 1 and the
-// P.V MFMAs of block 0.
+// The two blocks of a wave are software-pipelined (the band MFMAs of block 1
+// next to the softmax of block 0); the other wave on the SIMD fills the gaps.
 //
-// LDS: double-buffered K and V tiles, a ring of r rows (a tile uses 320 rows;
-// the 64 rows the next tile adds go into the free quarter), one skew buffer
-// per wave.  Tiles move HBM -> LDS with direct-to-LDS loads issued one tile
-// ahead; rows are 16-byte chunks with an XOR swizzle so that the 16 lanes of a
-// fragment read hit distinct banks.
+// LDS: double-buffered K and V tiles, two rings of r rows (one per end of the
+// paired query range; a tile needs three 64-row quarters of each, a fourth
+// loads ahead), one skew buffer per wave.  Tiles move HBM -> LDS with
+// direct-to-LDS loads issued one tile ahead; rows are 16-byte chunks with an
+// XOR swizzle so that the 16 lanes of a fragment read hit distinct banks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -58,14 +65,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DH = 64;
 constexpr int NW = 8;            // waves per workgroup (two per SIMD)
-constexpr int RB = 2;            // 16-query blocks per wave
-constexpr int BQ = NW * RB * 16; // queries per workgroup
+constexpr int RUNQ = 32;         // queries per run (two 16-query blocks)
+constexpr int NX = 2;            // 16-query blocks per wave (one run)
+constexpr int PAIRS = 4;         // run pairs per workgroup (waves w and w + 4 share a SIMD)
 constexpr int BK = 64;           // keys per tile
 constexpr int NT = BK / 16;      // 16-key sub-tiles per tile
 constexpr int NBT = NT + 1;      // band tiles per 16-query block
-constexpr int NWB = NT + RB;     // band tiles per wave
-constexpr int NQ = (BQ + BK - 1 + 63) / 64 + 1;   // ring quarters: those a tile uses plus one loading
-constexpr int RING = 64 * NQ;    // r rows held in LDS
+constexpr int NRB = NT + 2;      // band tiles per run (two blocks)
+constexpr int RQ = 4;            // ring quarters: three in use plus one loading
 constexpr int SROW = 84;         // skew buffer row stride (floats)
 constexpr int SKEW = 16 * SROW + 16;
 constexpr int CPR = DH / 8;      // 16-byte chunks per row
@@ -73,22 +80,22 @@ constexpr int RP = 16 / CPR;     // rows per 256 bytes
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
 constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
 constexpr int TILE_CH = BK * CPR;              // chunks per K or V tile (and per ring quarter)
+constexpr int NTHR = NW * 64;
+constexpr int LPT = TILE_CH / NTHR;            // 16-byte loads per thread per tile
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float TAU = 8.0f;      // deferred-rescale threshold (log2 units)
-static_assert(BQ + BK <= RING - 64, "ring must have a free quarter");
-static_assert(TILE_CH == NW * 64, "one 16-byte chunk of each tile per thread");
+static_assert(RUNQ * (PAIRS - 1) + 16 * NRB <= 64 * (RQ - 1), "a ring must hold one tile's bands in RQ - 1 quarters");
+static_assert(LPT * NTHR == TILE_CH, "whole tiles per load round");
 
 // Swizzle of chunk c in row r: K and r rows (16-row b128 fragment reads), V
 // rows (transposing b64 reads of 4 rows x 32 bytes).
 __device__ __forceinline__ int swz_k(int r) { return ((unsigned)r / RP) & (CPR - 1); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 6) & (CPR - 1); }
 
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Orders this wave's LDS accesses for the compiler without waiting: LDS
+// instructions of one wave execute in issue order, so a read issued after a
+// write sees it, also when another lane wrote it.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t x16) { return __uint_as_float(x16 << 16); }
 
@@ -140,46 +147,72 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-struct Tile {
-    bool first;  // first tile of this key range
-    const u32x4 *sk, *sv, *sr;
-    float *skw;
-    int kt;      // key tile index (selects the ring quarters)
-    int wband;   // first row of this wave's band inside the workgroup band
-    int j0, wq0, M;
+template <int X> using IC = std::integral_constant<int, X>;
+
+// Per-wave state of the two query blocks of the wave's run.
+struct State {
+    bf16x8 qu[NX][NKK], qv[NX][NKK];   // c (q + u), c (q + vb): B operands, lane (g, n) = query n
+    f32x4 o[NX][NDT];                   // O^T accumulators (unnormalised)
+    f32x4 lsum[NX];                     // softmax denominators (all 4 entries equal)
+    float mneg[NX];                     // -m: initial accumulator value of the band MFMA
+    float mref[NX];                     // running max (log2 units)
 };
 
-// Per-wave state carried across key tiles.
-struct State {
-    bf16x8 qu[RB][NKK], qv[RB][NKK];   // c (q + u), c (q + vb): B operands, lane (g, n) = query n
-    f32x4 o[RB][NDT];                   // O^T accumulators (unnormalised)
-    f32x4 lsum[RB];                     // softmax denominators (all 4 entries equal)
-    float mneg[RB];                     // -m: initial accumulator value of the band MFMA
-    float mref[RB];                     // running max (log2 units)
-    int klo[RB];                        // first visible key of this lane's query (lower bound)
+// Per-tile, wave-uniform description of one block.
+struct Blk {
+    int thi;    // band rows above thi are masked (causal bound)
+    int tlo;    // band rows below tlo are masked (same_length window)
+    int kmem;   // keys below kmem (tile-relative) are masked (per-row memory validity)
+};
+
+struct Tile {
+    const u32x4 *sk, *sv, *sr;
+    float *skw;         // this wave's skew buffer
+    int kt;             // key tile index (selects the ring quarters)
+    int offr;           // ring row offset of the run's band tile 0
+    bool first;         // first tile of the key range
 };
 
 // LOWER: some query has a lower key bound (window or memory validity), so a
 // query's first visible tile need not be the first tile of the range.
-template <bool MASK, bool LOWER>
-__device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n)
+// MASKED: some key of the run is masked on this tile (band rows or key
+// columns); otherwise every band row starts at -m.
+template <bool LOWER, bool MASKED>
+__device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, int n)
 {
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-    const int d0 = 4 * g - n;   // key offset minus query offset of this lane
 
-    // K fragments (A operands of the content MFMA)
-    auto load_k = [&](bf16x8 (&kf)[NT][NKK]) {
+    // Lane part of a fragment read: row n of a 16-row group, chunk (4 kk + g)
+    // under the row swizzle, which only depends on n for rows 16 apart.
+    int lane_ch[NKK];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int krow = 16 * tt + n;
+    for (int kk = 0; kk < NKK; ++kk) lane_ch[kk] = n * CPR + ((4 * kk + g) ^ swz_k(n));
+    // K fragments (A operands of the content MFMA), shared by the two blocks
+    bf16x8 kf[NT][NKK];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                kf[tt][kk] = __builtin_bit_cast(bf16x8, t.sk[krow * CPR + ((4 * kk + g) ^ swz_k(krow))]);
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            kf[tt][kk] = __builtin_bit_cast(bf16x8, t.sk[16 * tt * CPR + lane_ch[kk]]);
+    // r fragments of one run: run band tile u holds ring rows offr + 16 u + n.
+    // A 16-row band tile never straddles a 64-row quarter (offr is a multiple
+    // of 32), so its quarter slot is uniform across the wave.
+    bf16x8 rf[NRB][NKK];
+    auto load_r = [&]() {
+        const u32x4 *sr = t.sr;
+        const int offr = t.offr;
+#pragma unroll
+        for (int u = 0; u < NRB; ++u) {
+            const int x0 = offr + 16 * u;   // wave-uniform
+            const int ubase = ((t.kt + (x0 >> 6)) & (RQ - 1)) * TILE_CH + (x0 & 63) * CPR;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = __builtin_bit_cast(bf16x8, sr[ubase + lane_ch[kk]]);
         }
     };
     // V^T fragments (A operands of P.V), read through the transposing LDS read
-    auto load_v = [&](bf16x8 (&vf)[NT / 2][NDT]) {
+    bf16x8 vf[NT / 2][NDT];
+    auto load_v = [&]() {
         LDS_AS char *vb = (LDS_AS char *)(LDS_AS void *)t.sv;
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch)
@@ -197,168 +230,199 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, int g, int n
                 vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
             }
     };
-    bf16x8 rf[NWB][NKK];
-    auto load_r = [&](int wb) {
-        // workgroup band row x = wband + 16 wb + n lives in ring quarter (kt + x / 64) % NQ
-        const int x0 = t.wband + 16 * wb;
-        const int rrow = ((t.kt + (x0 >> 6)) % NQ) * 64 + (x0 & 63) + n;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            rf[wb][kk] = __builtin_bit_cast(bf16x8, t.sr[rrow * CPR + ((4 * kk + g) ^ swz_k(rrow))]);
-    };
 
-    f32x4 sc[RB][NT];
-    bf16x8 pf[RB][NT / 2];
+    f32x4 sc[NX][NT];
+    bf16x8 pf[NX][NT / 2];
 
-    // band MFMA of block rb (wave band tiles RB-1-rb .. RB-1-rb+NT) and skew into LDS
-    auto stage_a = [&](int rb) {
-        // all fragment reads first, then the five chains interleaved, then the skew writes
+    // A: band MFMA of block x (run band tiles 1-h .. 5-h) and skew into LDS
+    auto stage_a = [&](auto X) {
+        constexpr int x = decltype(X)::value;
+        constexpr int h = x & 1;
+        float *skw = t.skw;
+        const bf16x8 *qv = st.qv[x];
+        const float m = st.mneg[x];
+        f32x4 cin[NBT];
+        if constexpr (MASKED) {
+            // band row 16 bt + 4 g + v is visible iff tlo <= row <= thi
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) load_r(bt + (RB - 1) - rb);
-        const f32x4 m4 = {st.mneg[rb], st.mneg[rb], st.mneg[rb], st.mneg[rb]};
+            for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * bt + 4 * g + v;
+                    cin[bt][v] = (row > bk[x].thi || row < bk[x].tlo) ? -INFINITY : m;
+                }
+        } else {
+            const f32x4 m4 = {m, m, m, m};
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) cin[bt] = m4;
+        }
         f32x4 acc[NBT];
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + (RB - 1) - rb][0], st.qv[rb][0], m4);
+        for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + 1 - h][0], qv[0], cin[bt]);
 #pragma unroll
         for (int kk = 1; kk < NKK; ++kk)
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + (RB - 1) - rb][kk], st.qv[rb][kk], acc[bt]);
+            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + 1 - h][kk], qv[kk], acc[bt]);
+        lds_order();
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
             // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
-            float *dst = t.skw + n * (SROW + 1) + 16 * bt + 4 * g + 1;
+            float *dst = skw + n * (SROW + 1) + 16 * bt + 4 * g + 1;
             dst[0] = acc[bt][0];
             dst[1] = acc[bt][1];
             dst[2] = acc[bt][2];
             dst[3] = acc[bt][3];
         }
-        wave_lds_sync();
+        lds_order();
     };
-    // content MFMA of block rb on top of the skewed band values
-    auto stage_b = [&](int rb) {
-        bf16x8 kf[NT][NKK];
-        load_k(kf);
+    // B: content MFMA of block x on top of the skewed band values
+    auto stage_b = [&](auto X) {
+        constexpr int x = decltype(X)::value;
+        const float *skw = t.skw;
+        f32x4 cin[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 acc = *reinterpret_cast<const f32x4 *>(t.skw + n * SROW + 16 + 16 * tt + 4 * g);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = mfma(kf[tt][kk], st.qu[rb][kk], acc);
-            sc[rb][tt] = acc;
-        }
-        wave_lds_sync();
-    };
-    // mask, overflow check (rare rescale)
-    auto stage_check = [&](int rb) {
-        if constexpr (MASK) {
-            const int thr = t.M + t.wq0 + 16 * rb - t.j0;   // visible iff 16 tt + v + d0 <= thr
-            const int thl = LOWER ? st.klo[rb] - t.j0 - 4 * g : 0;   // and 16 tt + v >= thl
+        for (int tt = 0; tt < NT; ++tt)
+            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + n * SROW + 16 + 16 * tt + 4 * g);
+        lds_order();
+        if (LOWER && MASKED) {
+            // keys below kmem are hidden from every query of the block
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (16 * tt + v + d0 > thr || (LOWER && 16 * tt + v < thl)) sc[rb][tt][v] = -INFINITY;
+                    if (16 * tt + 4 * g + v < bk[x].kmem) cin[tt][v] = -INFINITY;
         }
-        float mx = max3(sc[rb][0][0], sc[rb][0][1], sc[rb][0][2]);
-        mx = max3(mx, sc[rb][0][3], sc[rb][1][0]);
-        mx = max3(mx, sc[rb][1][1], sc[rb][1][2]);
-        mx = max3(mx, sc[rb][1][3], sc[rb][2][0]);
-        mx = max3(mx, sc[rb][2][1], sc[rb][2][2]);
-        mx = max3(mx, sc[rb][2][3], sc[rb][3][0]);
-        mx = max3(mx, sc[rb][3][1], sc[rb][3][2]);
-        mx = fmaxf(mx, sc[rb][3][3]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 acc = cin[tt];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) acc = mfma(kf[tt][kk], st.qu[x][kk], acc);
+            sc[x][tt] = acc;
+        }
+    };
+    // C: overflow check (rare rescale), probabilities as bf16 B fragments
+    auto stage_c = [&](auto X) {
+        constexpr int x = decltype(X)::value;
+        float mx = max3(sc[x][0][0], sc[x][0][1], sc[x][0][2]);
+        mx = max3(mx, sc[x][0][3], sc[x][1][0]);
+        mx = max3(mx, sc[x][1][1], sc[x][1][2]);
+        mx = max3(mx, sc[x][1][3], sc[x][2][0]);
+        mx = max3(mx, sc[x][2][1], sc[x][2][2]);
+        mx = max3(mx, sc[x][2][3], sc[x][3][0]);
+        mx = max3(mx, sc[x][3][1], sc[x][3][2]);
+        mx = fmaxf(mx, sc[x][3][3]);
         // A query that has not seen a visible key yet takes the exact max of its
         // first visible tile; afterwards the max is only raised when a score
         // exceeds it by more than TAU.  Without lower key bounds that tile is
         // the first tile of the range; with them, a query is fresh while its
         // denominator is still empty.
-        const bool fresh = LOWER ? st.lsum[rb][0] == 0.f : t.first;
+        const bool fresh = LOWER ? st.lsum[x][0] == 0.f : t.first;
         if ((!LOWER && t.first) ||
             __builtin_amdgcn_ballot_w64(mx > TAU || (LOWER && fresh && mx != -INFINITY)) != 0) {
             const float rmx = row_max4(mx);
             float dlt;
             if (fresh) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the first visible tile
             else dlt = fmaxf(rmx, 0.f);                         // only ever raised
-            st.mref[rb] += dlt;
-            st.mneg[rb] -= dlt;
+            st.mref[x] += dlt;
+            st.mneg[x] -= dlt;
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) sc[rb][tt] -= dlt;
+            for (int tt = 0; tt < NT; ++tt) sc[x][tt] -= dlt;
             const float alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(-dlt);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] *= alpha;
-            st.lsum[rb] *= alpha;
+            for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] *= alpha;
+            st.lsum[x] *= alpha;
         }
-    };
-    // probabilities as bf16 B fragments
-    auto stage_c = [&](int rb) {
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch) {
             f32x8 p8;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                p8[v] = __builtin_amdgcn_exp2f(sc[rb][2 * ch][v]);
-                p8[4 + v] = __builtin_amdgcn_exp2f(sc[rb][2 * ch + 1][v]);
+                p8[v] = __builtin_amdgcn_exp2f(sc[x][2 * ch][v]);
+                p8[4 + v] = __builtin_amdgcn_exp2f(sc[x][2 * ch + 1][v]);
             }
-            pf[rb][ch] = __builtin_convertvector(p8, bf16x8);
+            pf[x][ch] = __builtin_convertvector(p8, bf16x8);
         }
     };
-    // O^T += V^T . P^T, denominator += ones . P^T
-    auto stage_d = [&](int rb) {
-        bf16x8 vf[NT / 2][NDT];
-        load_v(vf);
+    // D: O^T += V^T . P^T, denominator += ones . P^T
+    auto stage_d = [&](auto X) {
+        constexpr int x = decltype(X)::value;
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] = mfma(vf[ch][dt], pf[rb][ch], st.o[rb][dt]);
-            st.lsum[rb] = mfma(ones, pf[rb][ch], st.lsum[rb]);
+            for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = mfma(vf[ch][dt], pf[x][ch], st.o[x][dt]);
+            st.lsum[x] = mfma(ones, pf[x][ch], st.lsum[x]);
         }
     };
 
-    stage_a(0);
-    stage_b(0);
-    stage_check(0);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        stage_c(rb);
-        if (rb + 1 < RB) {
-            stage_a(rb + 1);
-            stage_b(rb + 1);
-        }
-        stage_d(rb);
-        if (rb + 1 < RB) stage_check(rb + 1);
-    }
+    // Pipeline over the two blocks (one skew buffer: block 1's band goes in
+    // after block 0's content stage has read it back; K and V fragments are
+    // never live together).  The scheduling barriers keep the stage order.
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    load_r();
+    stage_a(IC<0>{});
+    stage_b(IC<0>{});
+    fence();
+    stage_a(IC<1>{});
+    stage_c(IC<0>{});
+    stage_b(IC<1>{});
+    fence();
+    load_v();
+    stage_d(IC<0>{});
+    stage_c(IC<1>{});
+    stage_d(IC<1>{});
 }
 
 template <bool LOWER>
-__global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a)
+__global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 {
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 sr[RING * CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 sr[2][RQ * TILE_CH];
     __shared__ __attribute__((aligned(16))) float sskew[NW][SKEW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
 
-    // ---- which (query block, b*h, key split) this workgroup owns
+    // ---- which (pair group, b*h, key split) this workgroup owns
     const int BH = a.B * a.H;
     const int w = blockIdx.x;
     int slot = w, xg = 0, G = BH;
     if (a.remap) { xg = w & 7; slot = w >> 3; G = BH >> 3; }
     const int per = a.nsplit;
-    const int qb_rank = slot / (G * per);
-    const int r2 = slot - qb_rank * G * per;
+    const int grp = slot / (G * per);
+    const int r2 = slot - grp * G * per;
     const int bh = xg * G + r2 / per;
     const int split = r2 % per;
-    const int qb = a.nqb - 1 - qb_rank;   // longest query blocks first
     const int b = bh / a.H, h = bh - b * a.H;
     const int L = a.L, M = a.M, K = a.K;
-    const int i0 = qb * BQ;
-    const int kv_end = min(i0 + BQ, L) + M;
-    const int ntile = (kv_end + BK - 1) / BK;
-    // keys below the first query's lower bound are hidden from the whole block
-    const int kt0 = max(split * a.tiles_per_split, key_lo(a, b, i0) / BK);
+
+    // runs of 32 queries, paired from both ends
+    const int nr = (L + RUNQ - 1) / RUNQ;
+    const int npair = (nr + 1) / 2;
+    const int p0 = PAIRS * grp;
+    const int np = min(PAIRS, npair - p0);
+    // ring 0 holds the band rows of runs [p0, p0 + np), ring 1 those of runs
+    // [nr - p0 - np, nr - p0); ring row 0 of quarter q is r row cb + 64 q where
+    // cb belongs to the last (unclamped) query of the range and key 0.
+    const int ihi0 = RUNQ * (p0 + np) - 1;
+    const int ihi1 = RUNQ * (nr - p0) - 1;
+    const int cb0 = L - 1 - ihi0, cb1 = L - 1 - ihi1;
+    const int qmax = min(ihi1, L - 1);
+    const int ntile = (qmax + M + 1 + BK - 1) / BK;
+    int kt0 = split * a.tiles_per_split;
+    if (LOWER) kt0 = max(kt0, key_lo(a, b, RUNQ * p0) / BK);
     const int kt1 = min(ntile, split * a.tiles_per_split + a.tiles_per_split);
+
+    // this wave's run: waves w and w + 4 (one SIMD) take runs p and nr - 1 - p
+    // of pair p = p0 + w % 4 (one run if they coincide)
+    const int end = wave >> 2;
+    const int p = p0 + (wave & 3);
+    const int run = end == 0 ? p : nr - 1 - p;
+    const bool run_ok = (wave & 3) < np && (end == 0 || nr - 1 - p > p);
+    int i0[NX];
+#pragma unroll
+    for (int x = 0; x < NX; ++x) i0[x] = RUNQ * run + 16 * x;
 
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1];
     const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
@@ -366,49 +430,47 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
     const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + h * a.rs[0];
     const float *up = a.u + h * DH;
     const float *wp = a.vb + h * DH;
-    const int c_base = L - i0 - BQ;   // first r row of the workgroup band at tile 0
     const float c = a.c;              // scale * log2(e)
-
-    // Wave w owns the 32 queries of block qblk; waves w and w + 4 share a SIMD
-    // and own blocks s and 7 - s, whose key ranges add up to the same length.
-    const int qblk = wave < NW / 2 ? wave : (3 * NW / 2 - 1) - wave;
-    const int wq0 = i0 + 16 * RB * qblk;                    // first query of the wave
-    const int wband = (BQ - 16 * RB) - 16 * RB * qblk;      // first row of its band in the workgroup band
 
     State st;
     // ---- query fragments: c (q + u) and c (q + vb), in fp32, rounded once to bf16
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int iq = wq0 + 16 * rb + n;
-        const bool ok = iq < L;
-        const int iqc = ok ? iq : L - 1;
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        const bool ok = run_ok && iq < L;
+        const int iqc = ok ? iq : 0;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const u32x4 raw = *reinterpret_cast<const u32x4 *>(qp + (int64_t)iqc * a.qs[2] + kk * 32 + 8 * g);
             f32x8 fu, fv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = bf16_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                const float xv = bf16_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
                 const int col = kk * 32 + 8 * g + e;
-                fu[e] = ok ? (x + up[col]) * c : 0.f;
-                fv[e] = ok ? (x + wp[col]) * c : 0.f;
+                const float uu = up[col], ww = wp[col];
+                fu[e] = ok ? (xv + uu) * c : 0.f;
+                fv[e] = ok ? (xv + ww) * c : 0.f;
             }
-            st.qu[rb][kk] = __builtin_convertvector(fu, bf16x8);
-            st.qv[rb][kk] = __builtin_convertvector(fv, bf16x8);
+            st.qu[x][kk] = __builtin_convertvector(fu, bf16x8);
+            st.qv[x][kk] = __builtin_convertvector(fv, bf16x8);
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.mneg[rb] = 0.f;
-        st.mref[rb] = 0.f;
-        st.klo[rb] = key_lo(a, b, iqc);
+        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.mneg[x] = 0.f;
+        st.mref[x] = 0.f;
     }
-    const int wlo_first = key_lo(a, b, wq0);                      // smallest lower bound of the wave
-    const int wlo_last = key_lo(a, b, min(wq0 + 16 * RB - 1, L - 1));   // largest
+    // per-row memory validity: keys below M - mem_valid[b] are hidden from every query
+    int kmem_abs = 0;
+    if (LOWER && a.mem_valid) {
+        int mv = a.mem_valid[b];
+        mv = mv < 0 ? 0 : (mv > M ? M : mv);
+        kmem_abs = M - mv;
+    }
 
-    // ---- direct loads: thread tid moves chunk tid of each tile (row tid / 8),
-    // reading the chunk the XOR swizzle puts at that LDS position.  Rows outside
-    // [0, K) read zeros.
+    // ---- direct loads: thread tid moves chunks tid and tid + 256 of each tile
+    // (rows tid / 8 and tid / 8 + 32), reading the chunk the XOR swizzle puts at
+    // that LDS position.  Rows outside [0, K) read zeros.
     const int lrow = (unsigned)tid / CPR;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
@@ -418,75 +480,130 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
     const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
     const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][wave * 64]));
     const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][wave * 64]));
-    const uint32_t sr_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[wave * 64]));
+    const uint32_t sr0_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0][wave * 64]));
+    const uint32_t sr1_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[1][wave * 64]));
     auto load_kv = [&](int kt) {
-        const int row = kt * BK + lrow;
         const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
-        load_lds16(krs, (uint32_t)(row * krow_b + kch), sk_base + boff);
-        load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + boff);
+#pragma unroll
+        for (int e = 0; e < LPT; ++e) {
+            const int row = kt * BK + lrow + e * (NTHR / CPR);
+            const uint32_t loff = boff + (uint32_t)e * (NTHR * 16);
+            load_lds16(krs, (uint32_t)(row * krow_b + kch), sk_base + loff);
+            load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + loff);
+        }
     };
-    // ring quarter t % NQ holds r rows c_base + 64 t .. +63 (the swizzle only
+    // ring quarter q % RQ holds r rows cb + 64 q .. +63 (the swizzle only
     // depends on the row within the quarter)
-    auto load_r_quarter = [&](int t) {
-        const int row = c_base + 64 * t + lrow;
-        load_lds16(rrs, (uint32_t)(row * rrow_b + kch), sr_base + (uint32_t)(t % NQ) * (TILE_CH * 16));
+    auto load_r_quarter = [&](int q) {
+        const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
+#pragma unroll
+        for (int e = 0; e < LPT; ++e) {
+            const int x = 64 * q + lrow + e * (NTHR / CPR);
+            const uint32_t loff = qoff + (uint32_t)e * (NTHR * 16);
+            load_lds16(rrs, (uint32_t)((cb0 + x) * rrow_b + kch), sr0_base + loff);
+            load_lds16(rrs, (uint32_t)((cb1 + x) * rrow_b + kch), sr1_base + loff);
+        }
     };
 
     if (kt0 < kt1) {
         load_kv(kt0);
 #pragma unroll
-        for (int q = 0; q < NQ - 1; ++q) load_r_quarter(kt0 + q);
+        for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = kt0; kt < kt1; ++kt) {
+    Tile t;
+    t.sr = sr[end];
+    t.skw = sskew[wave];
+    t.offr = (end == 0 ? ihi0 : ihi1) - (RUNQ * run + RUNQ - 1);
+
+    // Tiles on which the run has a visible key: [ks, ke); within them, tiles on
+    // which no key of the run is masked: [us, ue).  Within the run's range one
+    // of its two blocks may see nothing; its band rows start at -inf.
+    int ks, ke, us = 0, ue;
+    {
+        const int ifirst = RUNQ * run, ilast = min(ifirst + RUNQ - 1, L - 1);
+        ks = LOWER ? max(kt0, key_lo(a, b, ifirst) / BK) : kt0;
+        ke = min(kt1, (ilast + M) / BK + 1);
+        if (!run_ok || ifirst >= L) ke = ks;
+        // causal: every key of tile kt is visible to the run's first query iff
+        // 64 kt + 63 <= ifirst + M (queries past L are discarded, unmasked)
+        ue = (ifirst + M + 1) / BK;
+        if (LOWER) {
+            // window: band rows below tlo of the run's second block; memory validity: keys below kmem_abs
+            if (a.window > 0) us = max(us, (ifirst + 16 + M + 15 - a.window + BK) / BK);
+            us = max(us, (kmem_abs + BK - 1) / BK);
+        }
+    }
+
+    // one key tile: stage the next tile, compute this one, wait
+    auto step = [&](auto ACT, auto MC, int kt) {
+        constexpr bool ACTIVE = decltype(ACT)::value != 0;
+        constexpr bool MASKED = decltype(MC)::value != 0;
         const int j0 = kt * BK;
         if (kt + 1 < kt1) {
             load_kv(kt + 1);
-            load_r_quarter(kt + NQ - 1);
+            load_r_quarter(kt + RQ - 1);
         }
-        if (wq0 < L && j0 <= min(wq0 + 16 * RB - 1, L - 1) + M && j0 + BK - 1 >= wlo_first) {
-            Tile t;
+        if constexpr (ACTIVE) {
+            Blk bk[NX];
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                // band row cc of query n is key j0 + cc + n - 15: visible iff cc <= M + i0 - j0 + 15
+                bk[x].thi = i0[x] < L ? M + i0[x] - j0 + 15 : -1;   // ragged tail: nothing visible
+                bk[x].tlo = (LOWER && a.window > 0) ? i0[x] + M + 1 - a.window - j0 + 15 : -1;
+                bk[x].kmem = kmem_abs - j0;
+            }
             t.sk = sk[kt & 1];
             t.sv = sv[kt & 1];
-            t.sr = sr;
-            t.skw = &sskew[wave][0];
             t.kt = kt;
-            t.wband = wband;
-            t.j0 = j0;
-            t.wq0 = wq0;
-            t.M = M;
             t.first = (kt == kt0);
-            if (j0 + BK - 1 > wq0 + M || j0 < wlo_last) tile_body<true, LOWER>(st, t, g, n);
-            else tile_body<false, LOWER>(st, t, g, n);
+            tile_body<LOWER, MASKED>(st, t, bk, g, n);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
+    };
+    // Walk the tiles in segments of one kind (active, masks needed) so that
+    // each loop runs one instance of the tile body and the state stays in place.
+    for (int kt = kt0; kt < kt1;) {
+        const bool act = kt >= ks && kt < ke;
+        const bool mk = kt < us || kt >= ue;
+        int e = kt1;
+        if (ks > kt) e = min(e, ks);
+        if (ke > kt) e = min(e, ke);
+        if (us > kt) e = min(e, us);
+        if (ue > kt) e = min(e, ue);
+        if (act) {
+            if (mk) for (; kt < e; ++kt) step(IC<1>{}, IC<1>{}, kt);
+            else for (; kt < e; ++kt) step(IC<1>{}, IC<0>{}, kt);
+        } else {
+            for (; kt < e; ++kt) step(IC<0>{}, IC<0>{}, kt);
+        }
     }
 
     // ---- epilogue: lane (g, n) holds query n, head columns 16 dt + 4 g + v
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int iq = wq0 + 16 * rb + n;
-        if (iq >= L) continue;
-        const float l = st.lsum[rb][0];
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        if (!run_ok || iq >= L) continue;
+        const float l = st.lsum[x][0];
         if (a.nsplit == 1) {
             const float inv = 1.f / l;
             uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + b * a.os[0] + h * a.os[1] + (int64_t)iq * a.os[2];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x4 yb = __builtin_convertvector(st.o[rb][dt] * inv, bf16x4);
+                const bf16x4 yb = __builtin_convertvector(st.o[x][dt] * inv, bf16x4);
                 *reinterpret_cast<u32x2 *>(op + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yb);
             }
-            if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[rb] + __log2f(l)) * LN2;
+            if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
         } else {
             float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[rb][dt];
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[x][dt];
             if (g == 0) {
                 float *pm = a.part_ml + (((int64_t)split * BH + bh) * L + iq) * 2;
-                pm[0] = (l > 0.f) ? st.mref[rb] : -INFINITY;   // no visible key in this split
+                pm[0] = (l > 0.f) ? st.mref[x] : -INFINITY;   // no visible key in this split
                 pm[1] = l;
             }
         }
@@ -495,7 +612,12 @@ __global__ __launch_bounds__(NW * 64) void relattn_fwd_bf16_kernel(RelAttnArgs a
 
 }  // namespace
 
-int relattn_bf16_rows_per_block() { return BQ; }
+int relattn_bf16_groups_per_head(int L)
+{
+    const int nr = (L + RUNQ - 1) / RUNQ;
+    const int npair = (nr + 1) / 2;
+    return (npair + PAIRS - 1) / PAIRS;
+}
 
 bool relattn_bf16_supported(int dh) { return dh == DH; }
 
@@ -504,9 +626,9 @@ hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s)
     if (dh != DH) return hipErrorInvalidValue;
     const int blocks = a.nqb * a.B * a.H * a.nsplit;
     if (a.window > 0 || a.mem_valid)
-        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<true>, dim3(blocks), dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<true>, dim3(blocks), dim3(NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<false>, dim3(blocks), dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<false>, dim3(blocks), dim3(NTHR), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_relattn_combine(a, 1, dh, s);

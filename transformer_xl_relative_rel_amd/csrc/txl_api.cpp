@@ -76,14 +76,14 @@ Plan plan_relattn(const txl_relattn_desc &d)
     }
     if (!p.fast && d.dtype == TXL_BF16 && d.dh <= 64 && (int64_t)BH * ceil_div(d.L, 16 * txl::kWaves * 2) >= 256)
         p.rb = 2;
-    const int BQ = p.fast ? txl::relattn_bf16_rows_per_block() : 16 * txl::kWaves * p.rb;
-    p.nqb = ceil_div(d.L, BQ);
+    p.nqb = p.fast ? txl::relattn_bf16_groups_per_head(d.L) : ceil_div(d.L, 16 * txl::kWaves * p.rb);
     const int ntile = ceil_div(d.L + d.M, txl::kBK);   // tiles of the longest query block
     int nsplit = d.splits;
     if (nsplit <= 0) {
-        const int64_t base = (int64_t)p.nqb * BH;
+        // the throughput kernel holds one workgroup per CU, the generic one two
+        const int64_t base = (int64_t)p.nqb * BH, target = p.fast ? 256 : 512;
         nsplit = 1;
-        if (base < 256) nsplit = (int)std::min<int64_t>(ntile, (512 + base - 1) / base);
+        if (base < 256) nsplit = (int)std::min<int64_t>(ntile, (target + base - 1) / base);
         if (nsplit < 1) nsplit = 1;
     }
     if (nsplit > ntile) nsplit = ntile;
