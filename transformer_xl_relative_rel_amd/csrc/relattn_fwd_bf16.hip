@@ -73,8 +73,14 @@ constexpr int NT = BK / 16;      // 16-key sub-tiles per tile
 constexpr int NBT = NT + 1;      // band tiles per 16-query block
 constexpr int NRB = NT + 2;      // band tiles per run (two blocks)
 constexpr int RQ = 4;            // ring quarters: three in use plus one loading
-constexpr int SROW = 84;         // skew buffer row stride (floats)
-constexpr int SKEW = 16 * SROW + 16;
+// Skew buffer: row n (query n) starts at float 80 n + 12 (n / 4); it is
+// written at columns 1..95 and read at columns 16..79, and the rows are far
+// enough apart that no row's writes reach another row's read range.  With
+// these starts the 64 lanes of a skew store (row n, column c + n) and the
+// 16-lane groups of a skew load (row n, 16-byte aligned column) each hit 64
+// distinct banks.
+__device__ __forceinline__ int skew_row(int n) { return 80 * n + 12 * (n >> 2); }
+constexpr int SKEW = 80 * 15 + 12 * 3 + 96;   // floats per wave
 constexpr int CPR = DH / 8;      // 16-byte chunks per row
 constexpr int RP = 16 / CPR;     // rows per 256 bytes
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
@@ -180,6 +186,11 @@ struct Tile {
 template <bool LOWER, bool MASKED>
 __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, int n)
 {
+    // Lane ids made opaque here, so that the lane parts of fragment addresses
+    // and mask bounds are recomputed per tile (a few adds) instead of being
+    // hoisted out of the tile loop, where they would stay live in registers
+    // (and spill) across the whole loop.
+    asm volatile("" : "+v"(g), "+v"(n));
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
@@ -267,7 +278,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
             // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
-            float *dst = skw + n * (SROW + 1) + 16 * bt + 4 * g + 1;
+            float *dst = skw + skew_row(n) + 16 * bt + 4 * g + n + 1;
             dst[0] = acc[bt][0];
             dst[1] = acc[bt][1];
             dst[2] = acc[bt][2];
@@ -282,7 +293,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         f32x4 cin[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + n * SROW + 16 + 16 * tt + 4 * g);
+            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + skew_row(n) + 16 + 16 * tt + 4 * g);
         lds_order();
         if (LOWER && MASKED) {
             // keys below kmem are hidden from every query of the block
