@@ -54,6 +54,10 @@ hipError_t launch_relattn(const RelAttnArgs &a, int dtype, int dh, int rb, hipSt
 int relattn_bf16_groups_per_head(int L);
 bool relattn_bf16_supported(int dh);
 hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s);
+// bf16 streaming kernel (dh = 64, no lower key bounds): nqb = query runs per
+// head, one one-wave workgroup per (b*h, key split, run).
+int relattn_bf16_stream_runs(int L);
+hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t s);
 // Key-range combine used by both kernels when nsplit > 1.
 hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s);
 

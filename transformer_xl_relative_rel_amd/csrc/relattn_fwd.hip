@@ -438,27 +438,50 @@ __global__ __launch_bounds__(256) void relattn_fwd_kernel(RelAttnArgs a)
 
 // Combine the key-range partials of the split path in split order:
 //   m* = max_s m_s,  out = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
+// One wave per block; the loads of CH splits are issued together (they are
+// independent) so the combine pays one memory latency per CH splits, while
+// the sums still run in split order (bitwise deterministic).
 template <bool BF, int DH>
-__global__ __launch_bounds__(256) void relattn_combine_kernel(RelAttnArgs a)
+__global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
 {
     using T = typename Elem<BF>::T;
     constexpr int TPR = DH / 4;                     // threads per query row
+    constexpr int CH = 8;                           // splits loaded together
     const int BH = a.B * a.H;
-    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int64_t row = (int64_t)blockIdx.x * (64 / TPR) + threadIdx.x / TPR;
     const int c4 = (threadIdx.x % TPR) * 4;
     if (row >= (int64_t)BH * a.L) return;
     const int bh = (int)(row / a.L), iq = (int)(row - (int64_t)bh * a.L);
     const int b = bh / a.H, h = bh - b * a.H;
+    const int64_t sstride = (int64_t)BH * a.L;      // rows between consecutive splits
+    const int64_t r0 = (int64_t)bh * a.L + iq;
     float mstar = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[(((int64_t)s * BH + bh) * a.L + iq) * 2]);
+    for (int s0 = 0; s0 < a.nsplit; s0 += CH) {
+        float mv[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) mv[e] = (s0 + e < a.nsplit) ? a.part_ml[((s0 + e) * sstride + r0) * 2] : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) mstar = fmaxf(mstar, mv[e]);
+    }
     float den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.nsplit; ++s) {
-        const int64_t base = ((int64_t)s * BH + bh) * a.L + iq;
-        const float ms = a.part_ml[base * 2], ls = a.part_ml[base * 2 + 1];
-        const float wgt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mstar);
-        den += wgt * ls;
-        num += wgt * *reinterpret_cast<const f32x4 *>(a.part_o + base * DH + c4);
+    for (int s0 = 0; s0 < a.nsplit; s0 += CH) {
+        float ms[CH], ls[CH];
+        f32x4 os[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const bool ok = s0 + e < a.nsplit;
+            const int64_t base = (ok ? s0 + e : 0) * sstride + r0;
+            ms[e] = ok ? a.part_ml[base * 2] : -INFINITY;
+            ls[e] = ok ? a.part_ml[base * 2 + 1] : 0.f;
+            os[e] = ok ? *reinterpret_cast<const f32x4 *>(a.part_o + base * DH + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const float wgt = (ms[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[e] - mstar);
+            den += wgt * ls[e];
+            num += wgt * os[e];
+        }
     }
     f32x4 y = num * (1.f / den);
     T *op = reinterpret_cast<T *>(a.out) + b * a.os[0] + h * a.os[1] + (int64_t)iq * a.os[2] + c4;
@@ -486,17 +509,17 @@ hipError_t launch_one(const RelAttnArgs &a, hipStream_t s)
 hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s)
 {
     const int64_t rows = (int64_t)a.B * a.H * a.L;
-    const int rows_per_block = 256 / (dh / 4);
+    const int rows_per_block = 64 / (dh / 4);
     const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
     if (dtype == 1) {
-        if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), grid, dim3(256), 0, s, a);
-        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<true, 64>), grid, dim3(256), 0, s, a);
-        else if (dh == 128) hipLaunchKernelGGL((relattn_combine_kernel<true, 128>), grid, dim3(256), 0, s, a);
+        if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), grid, dim3(64), 0, s, a);
+        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<true, 64>), grid, dim3(64), 0, s, a);
+        else if (dh == 128) hipLaunchKernelGGL((relattn_combine_kernel<true, 128>), grid, dim3(64), 0, s, a);
         else return hipErrorInvalidValue;
     } else {
-        if (dh == 16) hipLaunchKernelGGL((relattn_combine_kernel<false, 16>), grid, dim3(256), 0, s, a);
-        else if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), grid, dim3(256), 0, s, a);
-        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), grid, dim3(256), 0, s, a);
+        if (dh == 16) hipLaunchKernelGGL((relattn_combine_kernel<false, 16>), grid, dim3(64), 0, s, a);
+        else if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), grid, dim3(64), 0, s, a);
+        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), grid, dim3(64), 0, s, a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

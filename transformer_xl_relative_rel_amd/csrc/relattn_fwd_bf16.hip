@@ -155,6 +155,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 template <int X> using IC = std::integral_constant<int, X>;
 
+// Query fragments of one 16-query block: qu = c (q + u), qv = c (q + vb),
+// added in fp32 and rounded once to bf16 (B operands: lane (g, n) holds query
+// i0 + n, head columns 32 kk + 8 g .. + 7).  u and vb of the head are loaded
+// once as 16-byte buffer loads (they do not depend on the query), so every
+// load is issued up front; queries at or past L get zero fragments.
+struct QBias {
+    f32x4 u[2][2], w[2][2];   // [kk][half]: u and vb at columns 32 kk + 8 g + 4 half .. + 3
+};
+
+__device__ __forceinline__ QBias load_qbias(const float *u_h, const float *vb_h, int g)
+{
+    const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u_h), 0, 64 * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(vb_h), 0, 64 * 4, 0x00020000);
+    QBias qb;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t off = (uint32_t)(32 * kk + 8 * g + 4 * hf) * 4;
+            qb.u[kk][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(urs, off, 0, 0));
+            qb.w[kk][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+        }
+    return qb;
+}
+
+__device__ __forceinline__ void query_frags(const uint16_t *qrow, bool ok, float c, const QBias &qb, int g,
+                                            bf16x8 (&qu)[2], bf16x8 (&qv)[2])
+{
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(qrow + kk * 32 + 8 * g);
+        f32x8 fu, fv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = __uint_as_float(((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu) << 16);
+            fu[e] = (xv + qb.u[kk][e >> 2][e & 3]) * c;
+            fv[e] = (xv + qb.w[kk][e >> 2][e & 3]) * c;
+        }
+        const bf16x8 zero = {};
+        qu[kk] = ok ? __builtin_convertvector(fu, bf16x8) : zero;
+        qv[kk] = ok ? __builtin_convertvector(fv, bf16x8) : zero;
+    }
+}
+
 // Per-wave state of the two query blocks of the wave's run.
 struct State {
     bf16x8 qu[NX][NKK], qv[NX][NKK];   // c (q + u), c (q + vb): B operands, lane (g, n) = query n
@@ -445,26 +489,13 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 
     State st;
     // ---- query fragments: c (q + u) and c (q + vb), in fp32, rounded once to bf16
+    const QBias qb = load_qbias(up, wp, g);
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
         const int iq = i0[x] + n;
         const bool ok = run_ok && iq < L;
         const int iqc = ok ? iq : 0;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 raw = *reinterpret_cast<const u32x4 *>(qp + (int64_t)iqc * a.qs[2] + kk * 32 + 8 * g);
-            f32x8 fu, fv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = bf16_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-                const int col = kk * 32 + 8 * g + e;
-                const float uu = up[col], ww = wp[col];
-                fu[e] = ok ? (xv + uu) * c : 0.f;
-                fv[e] = ok ? (xv + ww) * c : 0.f;
-            }
-            st.qu[x][kk] = __builtin_convertvector(fu, bf16x8);
-            st.qv[x][kk] = __builtin_convertvector(fv, bf16x8);
-        }
+        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -621,6 +652,287 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming path: short segments against a long memory (few query runs, many
+// keys).  One wave per workgroup owns one run of 32 queries and one chunk of
+// key tiles; the chunks of a run are merged by the split combine.  Waves do
+// not share tiles, so K and r fragments come straight from global memory into
+// registers (their lane layout is the MFMA operand layout), one tile ahead in
+// a second register set; only V goes through LDS, for the transposing read.
+// Same arithmetic as the throughput kernel (band MFMA + skew, exp2 domain,
+// deferred rescale, denominator MFMA); no lower key bounds.
+
+// V^T fragments of a 64-key V tile in LDS: vf[ch][dt] is the A operand of the
+// P.V MFMA for keys 32 ch .. 32 ch + 31 and head columns 16 dt .. 16 dt + 15.
+// Lane (g, n) gets V[32 ch + 4 g + e][16 dt + n] (transposing read of rows
+// 4 g .. 4 g + 3) and the rows 16 below.  The row swizzle only depends on
+// bits 1-2 of the row, which 32 ch and +16 leave alone.
+__device__ __forceinline__ void read_vt(bf16x8 (&vf)[NT / 2][NDT], const u32x4 *sv, int g, int n)
+{
+    LDS_AS char *vb = (LDS_AS char *)(LDS_AS void *)sv;
+    const int row0 = 4 * g + (n >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int chunk = 2 * dt + ((n >> 1) & 1);
+        const int off = (row0 * CPR + (chunk ^ swz_v(row0))) * 16 + 8 * (n & 1);
+#pragma unroll
+        for (int ch = 0; ch < NT / 2; ++ch) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off + ch * 32 * CPR * 16));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off + (ch * 32 + 16) * CPR * 16));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+        }
+    }
+}
+
+constexpr int SNV = TILE_CH / 64;   // 16-byte V loads per lane per tile
+
+struct StreamFrags {
+    bf16x8 kf[NT][NKK];    // K fragments of the tile
+    bf16x8 rf[NRB][NKK];   // r fragments of the run's band for the tile
+};
+
+__global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
+{
+    __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
+    __shared__ __attribute__((aligned(16))) float skw[SKEW];
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, n = lane & 15;
+    const int nruns = a.nqb;
+    const int w = blockIdx.x;
+    const int run = w % nruns;
+    const int rest = w / nruns;
+    const int split = rest % a.nsplit;
+    const int bh = rest / a.nsplit;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int BH = a.B * a.H;
+    const int L = a.L, M = a.M, K = a.K;
+    const int ifirst = RUNQ * run, ilast = min(ifirst + RUNQ - 1, L - 1);
+    const int ntile = (ilast + M) / BK + 1;
+    const int kt0 = split * a.tiles_per_split;
+    const int kt1 = min(ntile, kt0 + a.tiles_per_split);
+
+    const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1];
+    const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
+    const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v) + b * a.vs[0] + h * a.vs[1];
+    const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + h * a.rs[0];
+    const float *up = a.u + h * DH;
+    const float *wp = a.vb + h * DH;
+    const float c = a.c;
+    int i0[NX];
+#pragma unroll
+    for (int x = 0; x < NX; ++x) i0[x] = ifirst + 16 * x;
+
+    State st;
+    const QBias qb = load_qbias(up, wp, g);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        const bool ok = iq < L;
+        const int iqc = ok ? iq : 0;
+        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.mneg[x] = 0.f;
+        st.mref[x] = 0.f;
+    }
+
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
+    const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
+    const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
+    // r row of the run's band tile 0 at key tile 0 (below 0 for a ragged last
+    // run: those rows read zeros and only feed discarded query columns)
+    const int rbase0 = L - 1 - (ifirst + RUNQ - 1);
+    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][0]));
+    const int vrow0 = lane / CPR;
+    const int vch = ((lane & (CPR - 1)) ^ swz_v(vrow0)) * 16;   // swz_v is the same for rows 8 apart
+
+    auto issue = [&](int kt, StreamFrags &f) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                f.kf[tt][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    krs, (uint32_t)((kt * BK + 16 * tt + n) * krow_b + (32 * kk + 8 * g) * 2), 0, 0));
+#pragma unroll
+        for (int u = 0; u < NRB; ++u)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                f.rf[u][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rrs, (uint32_t)((rbase0 + kt * BK + 16 * u + n) * rrow_b + (32 * kk + 8 * g) * 2), 0, 0));
+        const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
+#pragma unroll
+        for (int e = 0; e < SNV; ++e)
+            load_lds16(vrs, (uint32_t)((kt * BK + vrow0 + 8 * e) * vrow_b + vch), sv_base + boff + (uint32_t)e * 1024);
+    };
+    constexpr int LOADS = NT * NKK + NRB * NKK + SNV;   // vector memory loads per tile
+
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    // one tile from fragments f (K and r in registers, V in sv[kt & 1])
+    auto tile = [&](int kt, const StreamFrags &f, bool masked) {
+        int gg = g, nn = n;
+        asm volatile("" : "+v"(gg), "+v"(nn));
+        const int j0 = kt * BK;
+        f32x4 sc[NX][NT];
+        bf16x8 pf[NX][NT / 2];
+        auto stage_a = [&](auto X) {
+            constexpr int x = decltype(X)::value;
+            const float m = st.mneg[x];
+            f32x4 cin[NBT];
+            if (masked) {
+                const int thi = i0[x] < L ? M + i0[x] - j0 + 15 : -1;
+                const int g4 = 4 * gg;
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) cin[bt][v] = (g4 > thi - 16 * bt - v) ? -INFINITY : m;
+            } else {
+                const f32x4 m4 = {m, m, m, m};
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt) cin[bt] = m4;
+            }
+            f32x4 acc[NBT];
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(f.rf[bt + 1 - x][0], st.qv[x][0], cin[bt]);
+#pragma unroll
+            for (int kk = 1; kk < NKK; ++kk)
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(f.rf[bt + 1 - x][kk], st.qv[x][kk], acc[bt]);
+            lds_order();
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) {
+                float *dst = skw + skew_row(nn) + 16 * bt + 4 * gg + nn + 1;
+                dst[0] = acc[bt][0];
+                dst[1] = acc[bt][1];
+                dst[2] = acc[bt][2];
+                dst[3] = acc[bt][3];
+            }
+            lds_order();
+        };
+        auto stage_b = [&](auto X) {
+            constexpr int x = decltype(X)::value;
+            f32x4 cin[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                cin[tt] = *reinterpret_cast<const f32x4 *>(skw + skew_row(nn) + 16 + 16 * tt + 4 * gg);
+            lds_order();
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 acc = cin[tt];
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) acc = mfma(f.kf[tt][kk], st.qu[x][kk], acc);
+                sc[x][tt] = acc;
+            }
+        };
+        auto stage_c = [&](auto X) {
+            constexpr int x = decltype(X)::value;
+            float mx = max3(sc[x][0][0], sc[x][0][1], sc[x][0][2]);
+            mx = max3(mx, sc[x][0][3], sc[x][1][0]);
+            mx = max3(mx, sc[x][1][1], sc[x][1][2]);
+            mx = max3(mx, sc[x][1][3], sc[x][2][0]);
+            mx = max3(mx, sc[x][2][1], sc[x][2][2]);
+            mx = max3(mx, sc[x][2][3], sc[x][3][0]);
+            mx = max3(mx, sc[x][3][1], sc[x][3][2]);
+            mx = fmaxf(mx, sc[x][3][3]);
+            const bool first = kt == kt0;
+            if (first || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
+                const float rmx = row_max4(mx);
+                float dlt;
+                if (first) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the chunk's first tile
+                else dlt = fmaxf(rmx, 0.f);                         // only ever raised
+                st.mref[x] += dlt;
+                st.mneg[x] -= dlt;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) sc[x][tt] -= dlt;
+                const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-dlt);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] *= alpha;
+                st.lsum[x] *= alpha;
+            }
+#pragma unroll
+            for (int ch = 0; ch < NT / 2; ++ch) {
+                f32x8 p8;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    p8[v] = __builtin_amdgcn_exp2f(sc[x][2 * ch][v]);
+                    p8[4 + v] = __builtin_amdgcn_exp2f(sc[x][2 * ch + 1][v]);
+                }
+                pf[x][ch] = __builtin_convertvector(p8, bf16x8);
+            }
+        };
+        stage_a(IC<0>{});
+        stage_b(IC<0>{});
+        stage_a(IC<1>{});
+        stage_c(IC<0>{});
+        stage_b(IC<1>{});
+        stage_c(IC<1>{});
+        bf16x8 vf[NT / 2][NDT];
+        read_vt(vf, sv[kt & 1], gg, nn);
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int ch = 0; ch < NT / 2; ++ch) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = mfma(vf[ch][dt], pf[x][ch], st.o[x][dt]);
+                st.lsum[x] = mfma(ones, pf[x][ch], st.lsum[x]);
+            }
+    };
+
+    // tiles with every key visible to the run's first query need no mask
+    const int ue = (ifirst + M + 1) / BK;
+    StreamFrags fa, fb;
+    if (kt0 < kt1) issue(kt0, fa);
+    for (int kt = kt0; kt < kt1; kt += 2) {
+        if (kt + 1 < kt1) {
+            issue(kt + 1, fb);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        tile(kt, fa, kt >= ue || ifirst + RUNQ - 1 >= L);
+        if (kt + 1 >= kt1) break;
+        if (kt + 2 < kt1) {
+            issue(kt + 2, fa);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        tile(kt + 1, fb, kt + 1 >= ue || ifirst + RUNQ - 1 >= L);
+    }
+
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        if (iq >= L) continue;
+        const float l = st.lsum[x][0];
+        if (a.nsplit == 1) {
+            const float inv = 1.f / l;
+            uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + b * a.os[0] + h * a.os[1] + (int64_t)iq * a.os[2];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const bf16x4 yb = __builtin_convertvector(st.o[x][dt] * inv, bf16x4);
+                *reinterpret_cast<u32x2 *>(op + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yb);
+            }
+            if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
+        } else {
+            // an empty chunk (or no visible key in it) leaves o = 0, l = 0 and writes m = -inf
+            float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[x][dt];
+            if (g == 0) {
+                float *pm = a.part_ml + (((int64_t)split * BH + bh) * L + iq) * 2;
+                pm[0] = (l > 0.f) ? st.mref[x] : -INFINITY;
+                pm[1] = l;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int relattn_bf16_groups_per_head(int L)
@@ -631,6 +943,18 @@ int relattn_bf16_groups_per_head(int L)
 }
 
 bool relattn_bf16_supported(int dh) { return dh == DH; }
+
+int relattn_bf16_stream_runs(int L) { return (L + RUNQ - 1) / RUNQ; }
+
+hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t s)
+{
+    if (dh != DH || a.window > 0 || a.mem_valid) return hipErrorInvalidValue;
+    const int blocks = a.nqb * a.B * a.H * a.nsplit;
+    hipLaunchKernelGGL(relattn_stream_bf16_kernel, dim3(blocks), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    return launch_relattn_combine(a, 1, dh, s);
+}
 
 hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s)
 {

@@ -54,9 +54,10 @@ Extent extent(const void *p, const int64_t *stride, const int *count, int ndim, 
 
 bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Rows per wave block choice and key-range split of the attention kernel.
+// Kernel choice and key-range split of the attention call.
 struct Plan {
     int fast;    // 1: bf16 throughput kernel, 0: generic kernel
+    int stream;  // 1: bf16 streaming kernel (short segment, long memory)
     int rb, nqb, nsplit, tps;
     size_t ws_bytes;
 };
@@ -76,14 +77,20 @@ Plan plan_relattn(const txl_relattn_desc &d)
     }
     if (!p.fast && d.dtype == TXL_BF16 && d.dh <= 64 && (int64_t)BH * ceil_div(d.L, 16 * txl::kWaves * 2) >= 256)
         p.rb = 2;
-    p.nqb = p.fast ? txl::relattn_bf16_groups_per_head(d.L) : ceil_div(d.L, 16 * txl::kWaves * p.rb);
+    // Short segments against the memory (few query runs per head, no lower key
+    // bounds) go to the streaming kernel: one wave per (run, key chunk).
+    p.stream = (p.fast && d.L <= 128 && d.window == 0 && !d.mem_valid) ? 1 : 0;
+    p.nqb = p.stream ? txl::relattn_bf16_stream_runs(d.L)
+                     : (p.fast ? txl::relattn_bf16_groups_per_head(d.L) : ceil_div(d.L, 16 * txl::kWaves * p.rb));
     const int ntile = ceil_div(d.L + d.M, txl::kBK);   // tiles of the longest query block
     int nsplit = d.splits;
     if (nsplit <= 0) {
-        // the throughput kernel holds one workgroup per CU, the generic one two
-        const int64_t base = (int64_t)p.nqb * BH, target = p.fast ? 256 : 512;
+        // the throughput kernel holds one workgroup per CU, the generic one two;
+        // the streaming kernel's one-wave workgroups several per CU
+        const int64_t base = (int64_t)p.nqb * BH;
         nsplit = 1;
-        if (base < 256) nsplit = (int)std::min<int64_t>(ntile, (target + base - 1) / base);
+        if (p.stream) nsplit = (int)std::min<int64_t>(ntile, (1536 + base - 1) / base);
+        else if (base < 256) nsplit = (int)std::min<int64_t>(ntile, ((p.fast ? 256 : 512) + base - 1) / base);
         if (nsplit < 1) nsplit = 1;
     }
     if (nsplit > ntile) nsplit = ntile;
@@ -247,8 +254,9 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     a.remap = ((d->B * d->H) % 8 == 0) ? 1 : 0;
     a.mem_valid = d->mem_valid;
     a.window = d->window;
-    hipError_t e = p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
-                          : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
+    hipError_t e = p.stream ? txl::launch_relattn_bf16_stream(a, d->dh, static_cast<hipStream_t>(stream))
+                   : p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
+                            : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn launch failed: %s", hipGetErrorString(e));
     return ok();
 }
