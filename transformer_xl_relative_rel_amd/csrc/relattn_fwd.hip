@@ -438,15 +438,16 @@ __global__ __launch_bounds__(256) void relattn_fwd_kernel(RelAttnArgs a)
 
 // Combine the key-range partials of the split path in split order:
 //   m* = max_s m_s,  out = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
-// One wave per block; the loads of CH splits are issued together (they are
-// independent) so the combine pays one memory latency per CH splits, while
-// the sums still run in split order (bitwise deterministic).
+// One pass over the splits in chunks of CH whose loads are issued together
+// (one memory latency per chunk); the running sums are rescaled when a chunk
+// raises the running max.  The order is fixed, so the result is bitwise
+// deterministic.  One wave per block.
 template <bool BF, int DH>
 __global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
 {
     using T = typename Elem<BF>::T;
     constexpr int TPR = DH / 4;                     // threads per query row
-    constexpr int CH = 8;                           // splits loaded together
+    constexpr int CH = 16;                          // splits loaded together
     const int BH = a.B * a.H;
     const int64_t row = (int64_t)blockIdx.x * (64 / TPR) + threadIdx.x / TPR;
     const int c4 = (threadIdx.x % TPR) * 4;
@@ -455,15 +456,7 @@ __global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
     const int b = bh / a.H, h = bh - b * a.H;
     const int64_t sstride = (int64_t)BH * a.L;      // rows between consecutive splits
     const int64_t r0 = (int64_t)bh * a.L + iq;
-    float mstar = -INFINITY;
-    for (int s0 = 0; s0 < a.nsplit; s0 += CH) {
-        float mv[CH];
-#pragma unroll
-        for (int e = 0; e < CH; ++e) mv[e] = (s0 + e < a.nsplit) ? a.part_ml[((s0 + e) * sstride + r0) * 2] : -INFINITY;
-#pragma unroll
-        for (int e = 0; e < CH; ++e) mstar = fmaxf(mstar, mv[e]);
-    }
-    float den = 0.f;
+    float mrun = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < a.nsplit; s0 += CH) {
         float ms[CH], ls[CH];
@@ -476,9 +469,18 @@ __global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
             ls[e] = ok ? a.part_ml[base * 2 + 1] : 0.f;
             os[e] = ok ? *reinterpret_cast<const f32x4 *>(a.part_o + base * DH + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        float mnew = mrun;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) mnew = fmaxf(mnew, ms[e]);
+        if (mnew != mrun && mrun != -INFINITY) {
+            const float sc = __builtin_amdgcn_exp2f(mrun - mnew);
+            den *= sc;
+            num *= sc;
+        }
+        mrun = mnew;
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
-            const float wgt = (ms[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[e] - mstar);
+            const float wgt = (ms[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[e] - mrun);
             den += wgt * ls[e];
             num += wgt * os[e];
         }
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
     } else {
         *reinterpret_cast<f32x4 *>(op) = y;
     }
-    if (a.lse && c4 == 0) a.lse[row] = (mstar + __log2f(den)) * LN2;
+    if (a.lse && c4 == 0) a.lse[row] = (mrun + __log2f(den)) * LN2;
 }
 
 template <bool BF, int DH, int RB>
