@@ -65,6 +65,8 @@ def _load():
         lib.txo_relattn_fwd_vis_range.argtypes = [_I, _I, _I, _I, _I, ctypes.c_double, _I,
                                                   ctypes.POINTER(_I)] + [_D] * 8 + [_I, _I]
         lib.txo_relattn_row_vis.argtypes = [_I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _I] + [_D] * 8
+        lib.txo_relattn_bwd_range.argtypes = [_I, _I, _I, _I, _I, ctypes.c_double, _I,
+                                              ctypes.POINTER(_I)] + [_D] * 13 + [_I, _I]
         lib.txo_mem_update.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I, _I, _I, _I, _I64, _I64, _I64]
         lib.txo_pos_emb.argtypes = [_I, _I, _I, _D]
         lib.txo_linear.argtypes = [_I, _I, _I, _D, _D, _D, _D]
@@ -73,7 +75,7 @@ def _load():
         lib.txo_layer_fwd_ex.argtypes = [_I] * 9 + [ctypes.POINTER(_I)] + [_D] * 15 + [ctypes.c_double, _D]
         for name in ("txo_visible_mask", "txo_visible_mask_same_length", "txo_rel_shift",
                      "txo_relattn_scores", "txo_relattn_fwd_range", "txo_relattn_row",
-                     "txo_relattn_fwd_vis_range", "txo_relattn_row_vis",
+                     "txo_relattn_fwd_vis_range", "txo_relattn_row_vis", "txo_relattn_bwd_range",
                      "txo_mem_update", "txo_pos_emb", "txo_linear", "txo_layer_norm", "txo_layer_fwd",
                      "txo_layer_fwd_ex"):
             getattr(lib, name).restype = _I
@@ -184,6 +186,61 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
         for t in ts:
             t.join()
     return out, lse
+
+
+def relattn_bwd(q, k, v, r, u, vb, dout, scale: float | None = None, threads: int = 1,
+                bh_range: tuple[int, int] | None = None, same_length: int = 0, mem_valid=None):
+    """Gradients of relattn_fwd's output (see txo_relattn_bwd_range).
+
+    Shapes as relattn_fwd; dout [B, H, L, dh] is the upstream gradient of out.
+    Returns a dict of float64 arrays: dq [B, H, L, dh], dk, dv [B, H, K, dh],
+    dr [H, K, dh], du, dvb [H, dh].  dr, du and dvb are the sums over the
+    batch rows (in b order) of the per-head contributions.  ``bh_range``
+    restricts the work to a slice of the flattened (b, h) index: heads outside
+    it contribute nothing (their dq, dk, dv stay zero).
+    """
+    q, k, v, r, u, vb, dout = map(_f64, (q, k, v, r, u, vb, dout))
+    B, H, L, dh = q.shape
+    K = k.shape[2]
+    M = K - L
+    assert M >= 0 and k.shape == (B, H, K, dh) and v.shape == (B, H, K, dh) and dout.shape == q.shape
+    assert r.shape == (H, K, dh) and u.shape == (H, dh) and vb.shape == (H, dh)
+    dq = np.zeros((B, H, L, dh))
+    dk = np.zeros((B, H, K, dh))
+    dv = np.zeros((B, H, K, dh))
+    dr_bh = np.zeros((B, H, K, dh))
+    du_bh = np.zeros((B, H, dh))
+    dvb_bh = np.zeros((B, H, dh))
+    lo, hi = (0, B * H) if bh_range is None else bh_range
+    sc = 0.0 if scale is None else float(scale)
+    mv = None
+    if mem_valid is not None:
+        mv = np.ascontiguousarray(np.asarray(mem_valid, dtype=np.int32))
+        assert mv.shape == (B,)
+    mvp = mv.ctypes.data_as(ctypes.POINTER(_I)) if mv is not None else None
+    lib = _load()
+
+    def run(a, b):
+        _check(lib.txo_relattn_bwd_range(B, H, L, M, dh, sc, int(same_length), mvp, _p(q), _p(k), _p(v), _p(r),
+                                         _p(u), _p(vb), _p(dout), _p(dq), _p(dk), _p(dv), _p(dr_bh), _p(du_bh),
+                                         _p(dvb_bh), a, b), "relattn_bwd")
+
+    if threads <= 1 or hi - lo <= 1:
+        run(lo, hi)
+    else:
+        n = min(threads, hi - lo)
+        cuts = [lo + (hi - lo) * t // n for t in range(n + 1)]
+        ts = [threading.Thread(target=run, args=(cuts[t], cuts[t + 1])) for t in range(n)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    dr, du, dvb = np.zeros((H, K, dh)), np.zeros((H, dh)), np.zeros((H, dh))
+    for b in range(B):
+        dr += dr_bh[b]
+        du += du_bh[b]
+        dvb += dvb_bh[b]
+    return {"dq": dq, "dk": dk, "dv": dv, "dr": dr, "du": du, "dvb": dvb}
 
 
 def relattn_row(q, k, v, r, u, vb, b: int, h: int, i: int, scale: float | None = None,

@@ -401,6 +401,123 @@ int txo_relattn_row(int H, int L, int M, int dh, double scale, int b, int h, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward (gradients of the attention above)                              */
+/* ------------------------------------------------------------------------ */
+
+/* Gradients of one head's attention output with respect to every input, by
+ * the chain rule on the definition used by the forward functions above (the
+ * pages print no backward; they fix the forward, and [XL] "Why Stop Gradient"
+ * fixes which paths carry a gradient at the layer level).  With
+ *   s_ij = (ac_ij + bd_ij) * scale   on visible pairs,
+ *   p_ij = exp(s_ij) / sum_k exp(s_ik),        out_i = sum_j p_ij v_j,
+ * and an upstream gradient dout_i:
+ *   dP_ij = dout_i . v_j
+ *   dS_ij = p_ij (dP_ij - sum_k p_ik dP_ik)    (softmax Jacobian)
+ *   g_ij  = dS_ij * scale                      (gradient of ac_ij and of bd_ij)
+ *   dq_i  = sum_j g_ij (k_j + r_c),  c = L-1-i+j  (q_i enters both terms)
+ *   du    = sum_{i,j} g_ij k_j,   dvb = sum_{i,j} g_ij r_c
+ *   dk_j  = sum_i g_ij (q_i + u),  dv_j = sum_i p_ij dout_i
+ *   dr_c  = sum over (i, j) with L-1-i+j = c of g_ij (q_i + vb).
+ * Masked pairs carry p = 0 and so no gradient.  Keys of the memory get dk and
+ * dv like any other key: stop-gradient detaches the memory states themselves,
+ * but a layer still needs these rows for its projection weights.
+ * Outputs of this head: dq [L][dh], dk, dv [K][dh] (written), dr [K][dh],
+ * du, dvb [dh] (written: this head's contribution only; the caller sums the
+ * batch rows of a head). */
+static void head_backward(int L, int M, int dh, double scale, const double *q, const double *k,
+                          const double *v, const double *r, const double *u, const double *vb,
+                          const double *dout, const double *S, double *P, double *dS,
+                          double *dq, double *dk, double *dv, double *dr, double *du, double *dvb)
+{
+    int K = M + L;
+    for (int i = 0; i < L; ++i) {
+        const double *s = S + (size_t)i * K;
+        double m = -INFINITY;
+        for (int j = 0; j < K; ++j) if (s[j] > m) m = s[j];
+        double l = 0.0;
+        for (int j = 0; j < K; ++j) l += (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+        for (int j = 0; j < K; ++j) P[(size_t)i * K + j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) / l;
+    }
+    for (int i = 0; i < L; ++i) {
+        double rowdot = 0.0;
+        for (int j = 0; j < K; ++j) {
+            double dp = 0.0;
+            for (int e = 0; e < dh; ++e) dp += dout[(size_t)i * dh + e] * v[(size_t)j * dh + e];
+            dS[(size_t)i * K + j] = dp;
+            rowdot += P[(size_t)i * K + j] * dp;
+        }
+        for (int j = 0; j < K; ++j)
+            dS[(size_t)i * K + j] = P[(size_t)i * K + j] * (dS[(size_t)i * K + j] - rowdot);
+    }
+    memset(dq, 0, (size_t)L * dh * sizeof(double));
+    memset(dk, 0, (size_t)K * dh * sizeof(double));
+    memset(dv, 0, (size_t)K * dh * sizeof(double));
+    memset(dr, 0, (size_t)K * dh * sizeof(double));
+    memset(du, 0, (size_t)dh * sizeof(double));
+    memset(dvb, 0, (size_t)dh * sizeof(double));
+    for (int i = 0; i < L; ++i)
+        for (int j = 0; j < K; ++j) {
+            double p = P[(size_t)i * K + j];
+            if (p == 0.0) continue;
+            double gij = dS[(size_t)i * K + j] * scale;
+            int c = L - 1 - i + j;
+            for (int e = 0; e < dh; ++e) {
+                double qe = q[(size_t)i * dh + e];
+                double ke = k[(size_t)j * dh + e], re = r[(size_t)c * dh + e];
+                dq[(size_t)i * dh + e] += gij * (ke + re);
+                du[e] += gij * ke;
+                dvb[e] += gij * re;
+                dk[(size_t)j * dh + e] += gij * (qe + u[e]);
+                dr[(size_t)c * dh + e] += gij * (qe + vb[e]);
+                dv[(size_t)j * dh + e] += p * dout[(size_t)i * dh + e];
+            }
+        }
+}
+
+/* Backward over the heads [bh_begin, bh_end) of the flattened (b, h) index,
+ * with the same mask options as txo_relattn_fwd_vis_range (same_len 0 = off,
+ * mem_valid NULL = all memory rows valid).  Layouts as the forward; dout
+ * [B][H][L][dh].  dq [B][H][L][dh] and dk, dv [B][H][K][dh] are written for
+ * the heads in range; dr_bh [B*H][K][dh] and du_bh, dvb_bh [B*H][dh] receive
+ * each head's own contribution (dr, du and dvb of head h are the sums of
+ * these over the batch rows b). */
+int txo_relattn_bwd_range(int B, int H, int L, int M, int dh, double scale, int same_len,
+                          const int *mem_valid, const double *q, const double *k, const double *v,
+                          const double *r, const double *u, const double *vb, const double *dout,
+                          double *dq, double *dk, double *dv, double *dr_bh, double *du_bh, double *dvb_bh,
+                          int bh_begin, int bh_end)
+{
+    if (B < 1 || H < 1 || L < 1 || M < 0 || dh < 1 || same_len < 0) return TXO_EINVAL;
+    if (bh_begin < 0 || bh_end > B * H || bh_begin > bh_end) return TXO_EINVAL;
+    if (mem_valid)
+        for (int b = 0; b < B; ++b)
+            if (mem_valid[b] < 0 || mem_valid[b] > M) return TXO_EINVAL;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)dh);
+    int K = M + L;
+    size_t n = (size_t)L * K;
+    double *S = (double *)malloc(n * sizeof(double));
+    double *P = (double *)malloc(n * sizeof(double));
+    double *dS = (double *)malloc(n * sizeof(double));
+    unsigned char *vis = (unsigned char *)malloc(n);
+    if (!S || !P || !dS || !vis) { free(S); free(P); free(dS); free(vis); return TXO_ENOMEM; }
+    int rc = TXO_OK;
+    for (int bh = bh_begin; bh < bh_end; ++bh) {
+        int b = bh / H, h = bh % H;
+        rc = head_visible(L, M, same_len, mem_valid ? mem_valid[b] : M, vis);
+        if (rc != TXO_OK) break;
+        const double *qh = q + (size_t)bh * L * dh, *kh = k + (size_t)bh * K * dh;
+        const double *vh = v + (size_t)bh * K * dh, *rh = r + (size_t)h * K * dh;
+        const double *uh = u + (size_t)h * dh, *wh = vb + (size_t)h * dh;
+        head_scores_vis(L, M, dh, scale, qh, kh, rh, uh, wh, vis, S);
+        head_backward(L, M, dh, scale, qh, kh, vh, rh, uh, wh, dout + (size_t)bh * L * dh, S, P, dS,
+                      dq + (size_t)bh * L * dh, dk + (size_t)bh * K * dh, dv + (size_t)bh * K * dh,
+                      dr_bh + (size_t)bh * K * dh, du_bh + (size_t)bh * dh, dvb_bh + (size_t)bh * dh);
+    }
+    free(S); free(P); free(dS); free(vis);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Memory update                                                            */
 /* ------------------------------------------------------------------------ */
 

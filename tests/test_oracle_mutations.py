@@ -35,6 +35,16 @@ MUTATIONS = [
      "for (int j = 0; j < M - mvalid + 1 && j < K; ++j) vis"),
     ("same_length_shift", "int lower = (j - i) <= -shift;", "int lower = (j - i) < -shift;"),
     ("layer_ignores_clamp", "txo_pos_emb(K, d, clamp_len, pe);", "txo_pos_emb(K, d, 0, pe);"),
+    ("bwd_dq_drops_position", "dq[(size_t)i * dh + e] += gij * (ke + re);", "dq[(size_t)i * dh + e] += gij * ke;"),
+    ("bwd_dk_drops_u", "dk[(size_t)j * dh + e] += gij * (qe + u[e]);", "dk[(size_t)j * dh + e] += gij * qe;"),
+    ("bwd_dr_reversed_rows", "dr[(size_t)c * dh + e] += gij * (qe + vb[e]);",
+     "dr[(size_t)(K - 1 - c) * dh + e] += gij * (qe + vb[e]);"),
+    ("bwd_no_softmax_centering", "P[(size_t)i * K + j] * (dS[(size_t)i * K + j] - rowdot);",
+     "P[(size_t)i * K + j] * (dS[(size_t)i * K + j]);"),
+    ("bwd_dv_from_g", "dv[(size_t)j * dh + e] += p * dout[(size_t)i * dh + e];",
+     "dv[(size_t)j * dh + e] += gij * dout[(size_t)i * dh + e];"),
+    ("bwd_scale_dropped", "double gij = dS[(size_t)i * K + j] * scale;", "double gij = dS[(size_t)i * K + j];"),
+    ("bwd_du_from_r", "du[e] += gij * ke;", "du[e] += gij * re;"),
 ]
 
 PINS = [
@@ -51,6 +61,9 @@ PINS = [
     lambda: pins.test_mem_valid_equals_truncated_memory(3),
     lambda: pins.test_same_length_rows_are_windows(6, 4, 4),
     lambda: pins.test_layer_options_match_torch_third_opinion(3, 0, None),
+    lambda: pins.test_backward_matches_finite_differences(1, 2, 5, 3, 4, 0, None),
+    lambda: pins.test_backward_matches_torch_autograd_of_literal_form(1, 2, 5, 3, 4),
+    pins.test_backward_closed_forms,
 ]
 
 

@@ -530,3 +530,114 @@ def test_stack_memory_holds_earlier_hidden_states():
             allh = np.concatenate(hist[n], axis=1)
             np.testing.assert_array_equal(new[n], allh[:, -min(M, allh.shape[1]):])
         mems = new
+
+
+# ---------------------------------------------------------------------------
+# Backward.  The pages fix the forward only; its gradients are fixed by the
+# mathematics.  Three independent routes pin the oracle's backward: finite
+# differences of the (pinned) forward oracle, torch autograd through the
+# pages' literal formulation ([SRC] RelPartialLearnableMultiHeadAttn.forward:
+# einsum, _rel_shift by pad / view, masked_fill, softmax), and closed forms.
+# ---------------------------------------------------------------------------
+
+BWD_KEYS = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("r", "dr"), ("u", "du"), ("vb", "dvb"))
+
+
+def _bwd_inputs(B, H, L, M, dh, seed):
+    rng = _rng(seed)
+    K = M + L
+    return dict(q=rng.normal(size=(B, H, L, dh)), k=rng.normal(size=(B, H, K, dh)),
+                v=rng.normal(size=(B, H, K, dh)), r=rng.normal(size=(H, K, dh)),
+                u=rng.normal(size=(H, dh)), vb=rng.normal(size=(H, dh))), rng.normal(size=(B, H, L, dh))
+
+
+@pytest.mark.parametrize("B,H,L,M,dh,same_length,mem_valid", [
+    (1, 2, 5, 3, 4, 0, None), (2, 1, 4, 0, 3, 0, None), (2, 2, 3, 6, 2, 0, None),
+    (1, 1, 6, 4, 3, 3, None), (2, 1, 4, 5, 2, 0, [2, 5]), (3, 1, 5, 4, 2, 6, [0, 4, 1])])
+def test_backward_matches_finite_differences(B, H, L, M, dh, same_length, mem_valid):
+    """Directional derivative of <dout, out> along a random direction of every
+    input: central difference of the forward oracle (error O(h^2) ~ 1e-10)
+    against <grad, direction>."""
+    x, dout = _bwd_inputs(B, H, L, M, dh, 100 + L + 7 * M)
+    g = oracle.relattn_bwd(**x, dout=dout, same_length=same_length, mem_valid=mem_valid)
+    rng = _rng(5)
+
+    def loss(**kw):
+        out, _ = oracle.relattn_fwd(**{**x, **kw}, same_length=same_length, mem_valid=mem_valid)
+        return float((out * dout).sum())
+
+    for name, key in BWD_KEYS:
+        e = rng.normal(size=x[name].shape)
+        h = 1e-5
+        fd = (loss(**{name: x[name] + h * e}) - loss(**{name: x[name] - h * e})) / (2 * h)
+        an = float((g[key] * e).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def _torch_literal_loss(t, dout, M):
+    """The pages' literal forward on one batch of heads, in torch fp64:
+    AC = einsum((q+u), k); BD_raw = einsum((q+vb), r); BD = pad / view / slice
+    ([SRC] _rel_shift); score = (AC + BD) * scale; masked_fill(-inf) with
+    triu(ones(L, K), 1 + M); softmax; P . V."""
+    q, k, v, r, u, vb = (t[n] for n in ("q", "k", "v", "r", "u", "vb"))
+    B, H, L, dh = q.shape
+    K = k.shape[2]
+    ac = torch.einsum("bhid,bhjd->bhij", q + u[None, :, None, :], k)
+    bd_raw = torch.einsum("bhid,hcd->bhic", q + vb[None, :, None, :], r)
+    padded = F.pad(bd_raw, (1, 0))                       # zero column in front
+    bd = padded.reshape(B, H, K + 1, L)[:, :, 1:].reshape(B, H, L, K)
+    s = (ac + bd) / math.sqrt(dh)
+    mask = torch.triu(torch.ones(L, K, dtype=torch.bool), diagonal=1 + M)
+    p = torch.softmax(s.masked_fill(mask, float("-inf")), dim=-1)
+    return (torch.einsum("bhij,bhjd->bhid", p, v) * dout).sum()
+
+
+@pytest.mark.parametrize("B,H,L,M,dh", [(1, 2, 5, 3, 4), (2, 1, 6, 0, 3), (1, 1, 4, 9, 2), (2, 2, 7, 7, 5)])
+def test_backward_matches_torch_autograd_of_literal_form(B, H, L, M, dh):
+    """Third opinion: torch autograd (fp64, CPU) through the literal pad / view
+    relative shift, against the oracle's direct-indexing backward."""
+    x, dout = _bwd_inputs(B, H, L, M, dh, 300 + L + M)
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in x.items()}
+    _torch_literal_loss(t, torch.tensor(dout), M).backward()
+    g = oracle.relattn_bwd(**x, dout=dout)
+    for name, key in BWD_KEYS:
+        np.testing.assert_allclose(g[key], t[name].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_closed_forms():
+    """(1) Softmax rows sum to 1, so sum_j dv_j = sum_i dout_i.  (2) With all
+    keys equal and all r rows equal, every score row is constant over its
+    visible keys, the softmax Jacobian annihilates it (sum_j dS_ij = 0), and
+    dq, du, dvb vanish.  (3) With dout = 0 every gradient is 0."""
+    B, H, L, M, dh = 2, 2, 6, 5, 4
+    x, dout = _bwd_inputs(B, H, L, M, dh, 11)
+    g = oracle.relattn_bwd(**x, dout=dout)
+    np.testing.assert_allclose(g["dv"].sum(axis=2), dout.sum(axis=2), rtol=1e-12, atol=1e-12)
+    y = dict(x)
+    y["k"] = np.broadcast_to(x["k"][:, :, :1], x["k"].shape).copy()
+    y["r"] = np.broadcast_to(x["r"][:, :1], x["r"].shape).copy()
+    g2 = oracle.relattn_bwd(**y, dout=dout)
+    for key in ("dq", "du", "dvb"):
+        assert np.abs(g2[key]).max() < 1e-12, key
+    g3 = oracle.relattn_bwd(**x, dout=np.zeros_like(dout))
+    for _, key in BWD_KEYS:
+        assert not np.any(g3[key]), key
+
+
+def test_backward_mem_valid_equals_truncated_memory():
+    """Hiding the oldest memory rows of a batch row gives that row the
+    gradients of attention over the shortened memory, and zero dk / dv on the
+    hidden rows ([XL] "Batched Streams": memory belongs to the row's stream)."""
+    B, H, L, M, dh = 2, 1, 4, 6, 3
+    x, dout = _bwd_inputs(B, H, L, M, dh, 21)
+    mv = [2, 6]
+    g = oracle.relattn_bwd(**x, dout=dout, mem_valid=mv)
+    for b in range(B):
+        cut = M - mv[b]
+        xb = dict(q=x["q"][b:b + 1], k=x["k"][b:b + 1, :, cut:], v=x["v"][b:b + 1, :, cut:], r=x["r"][:, cut:],
+                  u=x["u"], vb=x["vb"])
+        gb = oracle.relattn_bwd(**xb, dout=dout[b:b + 1])
+        np.testing.assert_allclose(g["dq"][b:b + 1], gb["dq"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g["dk"][b:b + 1, :, cut:], gb["dk"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g["dv"][b:b + 1, :, cut:], gb["dv"], rtol=1e-12, atol=1e-13)
+        assert not np.any(g["dk"][b, :, :cut]) and not np.any(g["dv"][b, :, :cut])
