@@ -128,6 +128,49 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *desc, const void *q, const vo
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Relative attention backward                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace txl_relattn_bwd needs for `desc` (always > 0:
+ * the prepared query operands, row constants and one bf16 [B][H][L][K']
+ * buffer of score gradients, K' = K rounded up to 64).  *bytes is written on
+ * success; the same errors as txl_relattn_bwd for an unsupported desc. */
+txl_status txl_relattn_bwd_workspace_size(const txl_relattn_desc *desc, size_t *bytes);
+
+/* Gradients of txl_relattn_fwd with respect to all of its inputs.
+ *
+ * The pages define the forward only ([SRC] RelPartialLearnableMultiHeadAttn
+ * .forward); these are its derivatives by the chain rule.  With the visible
+ * set, s_ij and p_ij = softmax_j(s_ij) of txl_relattn_fwd, the upstream
+ * gradient dout_i of out_i, dP_ij = dout_i . v_j and
+ * dS_ij = p_ij (dP_ij - sum_k p_ik dP_ik):
+ *   dq_i = scale sum_j dS_ij (k_j + r_k[L-1-i+j])
+ *   dk_j = scale sum_i dS_ij (q_i + u)          dv_j = sum_i p_ij dout_i
+ *   dr_k[c] = scale sum_{b, i, j: L-1-i+j = c} dS_ij (q_i + vb)
+ *   du = scale sum_{b,i,j} dS_ij k_j           dvb = scale sum_{b,i,j} dS_ij r_k[L-1-i+j]
+ * Masked pairs carry no gradient.  Memory keys (j < M) get dk and dv like the
+ * others: [XL] "Why Stop Gradient" detaches the cached memory states of a
+ * layer stack, which is the caller's business (it drops these rows when it
+ * propagates to the memory, and keeps them for the projection weights).
+ *
+ * Inputs: desc, q, k, v, r_k, u, vb exactly as passed to txl_relattn_fwd
+ * (same masks: window, mem_valid); out and lse (required) as it returned
+ * them; dout [B][H][L][dh] with desc->o_stride.  p is recomputed from lse.
+ * Outputs (caller-owned, fully overwritten):
+ *   dq [B][H][L][dh] with desc->q_stride, dk and dv [B][H][K][dh] with
+ *   desc->k_stride and desc->v_stride, all of `dtype`;
+ *   dr [H][K][dh] fp32 contiguous, du and dvb [H][dh] fp32 contiguous.
+ * Supported: dtype TXL_BF16 with dh = 64 (else TXL_ERR_UNSUPPORTED), one
+ * head's rows within 2 GiB.  Workspace: txl_relattn_bwd_workspace_size()
+ * bytes, 256-byte aligned.  No output may overlap an input, another output or
+ * the workspace (TXL_ERR_ALIAS).  Results are bitwise reproducible (fixed
+ * summation orders, no atomics).  desc->splits is ignored. */
+txl_status txl_relattn_bwd(const txl_relattn_desc *desc, const void *q, const void *k, const void *v,
+                           const void *r_k, const float *u, const float *vb, const void *out, const float *lse,
+                           const void *dout, void *dq, void *dk, void *dv, float *dr, float *du, float *dvb,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Memory update (Tail_M)                                                   */
 /* ------------------------------------------------------------------------ */
 

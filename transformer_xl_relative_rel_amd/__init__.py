@@ -11,7 +11,8 @@ import ctypes
 import os
 
 __all__ = [
-    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "mem_update", "mem_update_batched",
+    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "relattn_bwd",
+    "relattn_bwd_workspace_size", "mem_update", "mem_update_batched",
     "layer_fwd", "layer_workspace_size", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
 
@@ -22,7 +23,8 @@ _lib = None
 
 # Every function declared in include/txl.h.
 EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
-            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update", "txl_mem_update_batched",
+            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_bwd_workspace_size", "txl_relattn_bwd",
+            "txl_mem_update", "txl_mem_update_batched",
             "txl_layer_workspace_size", "txl_layer_fwd")
 
 # Weight names of one decoder layer, in the order of txl_layer_weights.
@@ -75,13 +77,16 @@ def lib():
     L.txl_relattn_desc_init.argtypes = [dp, i, i, i, i, i, i]
     L.txl_relattn_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     L.txl_relattn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.txl_relattn_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    L.txl_relattn_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
     L.txl_mem_update.argtypes = [vp, i, vp, i, vp, i, i, i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     L.txl_mem_update_batched.argtypes = [i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, ctypes.POINTER(vp), i, i,
                                          i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     ldp = ctypes.POINTER(LayerDesc)
     L.txl_layer_workspace_size.argtypes = [ldp, i, ctypes.POINTER(sz)]
     L.txl_layer_fwd.argtypes = [ldp, ctypes.POINTER(LayerWeights), vp, vp, i, vp, vp, vp, vp, sz, vp]
-    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_mem_update",
+    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd",
+                 "txl_relattn_bwd_workspace_size", "txl_relattn_bwd", "txl_mem_update",
                  "txl_mem_update_batched", "txl_layer_workspace_size", "txl_layer_fwd"):
         getattr(L, name).restype = i
     _lib = L
@@ -176,6 +181,71 @@ def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, ls
     _check(lib().txl_relattn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
                                  _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def _bwd_desc(q, k, v, r_k, out, dout, scale, window, mem_valid) -> RelAttnDesc:
+    import torch
+    if dout.stride() != out.stride() or dout.shape != out.shape:
+        raise ValueError("dout must have the shape and strides of out")
+    d = _desc(q, k, r_k, out, v, scale, 0)
+    d.window = int(window)
+    if mem_valid is not None:
+        if mem_valid.dtype != torch.int32 or not mem_valid.is_contiguous() or mem_valid.numel() != q.shape[0]:
+            raise ValueError("mem_valid must be a contiguous int32 tensor of B entries")
+        d.mem_valid = mem_valid.data_ptr()
+    return d
+
+
+def relattn_bwd_workspace_size(q, k, v, r_k, out, dout, window: int = 0, mem_valid=None) -> int:
+    """Workspace bytes txl_relattn_bwd needs for these tensors."""
+    d = _bwd_desc(q, k, v, r_k, out, dout, None, window, mem_valid)
+    n = ctypes.c_size_t(0)
+    _check(lib().txl_relattn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def relattn_bwd(q, k, v, r_k, u, vb, out, lse, dout, *, scale: float | None = None, window: int = 0,
+                mem_valid=None, dq=None, dk=None, dv=None, dr=None, du=None, dvb=None, workspace=None, stream=None):
+    """Gradients of relattn_fwd (txl_relattn_bwd): bf16, dh = 64.
+
+    q, k, v, r_k, u, vb, scale, window and mem_valid as given to relattn_fwd;
+    out and lse [B, H, L] float32 as it returned them; dout is the upstream
+    gradient of out (same shape and strides).  Returns (dq, dk, dv, dr, du,
+    dvb): dq, dk, dv like q, k, v (bf16), dr [H, K, dh], du and dvb [H, dh]
+    float32.  Output tensors may be passed in (dq, dk, dv with the strides of
+    q, k, v; the float32 ones contiguous).
+    """
+    import torch
+    for t in (u, vb, lse):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("u, vb and lse must be contiguous float32")
+    d = _bwd_desc(q, k, v, r_k, out, dout, scale, window, mem_valid)
+    H, K, dh = r_k.shape
+    dev = q.device
+    if dq is None:
+        dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    if dk is None:
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=dev)
+    if dv is None:
+        dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.stride() != ref.stride() or t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape and strides of {name[1:]}")
+    dr = torch.empty((H, K, dh), dtype=torch.float32, device=dev) if dr is None else dr
+    du = torch.empty((H, dh), dtype=torch.float32, device=dev) if du is None else du
+    dvb = torch.empty((H, dh), dtype=torch.float32, device=dev) if dvb is None else dvb
+    for t in (dr, du, dvb):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("dr, du and dvb must be contiguous float32")
+    need = ctypes.c_size_t(0)
+    _check(lib().txl_relattn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().txl_relattn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
+                                 _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dr), _ptr(du), _ptr(dvb),
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
+    return dq, dk, dv, dr, du, dvb
 
 
 def _new_len(M_cur: int, L: int, mem_len: int, ext_len: int) -> int:

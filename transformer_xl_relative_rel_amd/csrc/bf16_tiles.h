@@ -1,0 +1,121 @@
+// Small device helpers for the bf16 MFMA kernels of the attention backward:
+// 16x16x32 bf16 MFMA, direct-to-LDS buffer loads, LDS tile addressing with a
+// row-dependent chunk swizzle and the transposing LDS read.  Internal header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace txl {
+namespace tiles {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define TXL_LDS_AS __attribute__((address_space(3)))
+
+constexpr int DH = 64;             // head width of these kernels
+constexpr int CPR = DH / 8;        // 16-byte chunks per 64-element bf16 row
+constexpr float LN2 = 0.69314718055994530942f;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Chunk swizzle of an LDS tile of 64-element bf16 rows: chunk c of row r sits
+// at position c ^ swz(r).  Rows r and r + 1 share a pattern, so a 16-row
+// fragment read (16 lanes, one chunk each) spreads over all 8 positions.
+__device__ __forceinline__ int swz(int r) { return ((unsigned)r >> 1) & (CPR - 1); }
+
+// Orders this wave's LDS accesses for the compiler without waiting.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(TXL_LDS_AS const void *)p;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane: lane l writes LDS byte address
+// lds + 16 l (lds is wave-uniform).  Offsets at or past the resource size read
+// zeros.  Inline assembly, so the compiler does not track it: the caller waits
+// (s_waitcnt vmcnt(0), then a barrier) before anything reads the target.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "memory");
+}
+
+// 16-byte global load through a buffer resource (zeros past its size).
+__device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+}
+
+// Row fragment of an LDS tile (64-element bf16 rows, swizzled): the 8
+// elements 32 kk + 8 g .. + 7 of row `row` (A or B operand of a 16x16x32
+// MFMA whose contraction runs over the row).
+__device__ __forceinline__ bf16x8 row_frag(const u32x4 *tile, int row, int kk, int g)
+{
+    return __builtin_bit_cast(bf16x8, tile[row * CPR + ((4 * kk + g) ^ swz(row))]);
+}
+
+// Column fragment through the transposing LDS read: for lane (g, n) the
+// elements [rows rb + 4 g + e][col 16 dt + n] (e = 0..3, k-slots 0..3) and
+// [rows rb + 16 + 4 g + e][same col] (k-slots 4..7).  This is the operand
+// layout of a 16x16x32 MFMA whose contraction runs over 32 tile rows taken
+// in the order {4g..4g+3, 16+4g..16+4g+3} per lane group; a C-layout result
+// of two 16-row MFMA tiles packs into the matching B/A operand without data
+// movement.  rb must be a multiple of 4.
+__device__ __forceinline__ bf16x8 col_frag(const u32x4 *tile, int rb, int dt, int g, int n)
+{
+    TXL_LDS_AS char *base = (TXL_LDS_AS char *)(TXL_LDS_AS void *)tile;
+    const int chunk = 2 * dt + ((n >> 1) & 1);
+    const int r0 = rb + 4 * g + (n >> 2), r1 = r0 + 16;
+    const int off0 = (r0 * CPR + (chunk ^ swz(r0))) * 16 + 8 * (n & 1);
+    const int off1 = (r1 * CPR + (chunk ^ swz(r1))) * 16 + 8 * (n & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(base + off0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(base + off1));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
+// Half of col_frag: rows rb + 4 g + e only (k-slots 0..3); k-slots 4..7 zero.
+__device__ __forceinline__ bf16x8 col_frag_lo(const u32x4 *tile, int rb, int dt, int g, int n)
+{
+    TXL_LDS_AS char *base = (TXL_LDS_AS char *)(TXL_LDS_AS void *)tile;
+    const int chunk = 2 * dt + ((n >> 1) & 1);
+    const int r0 = rb + 4 * g + (n >> 2);
+    const int off0 = (r0 * CPR + (chunk ^ swz(r0))) * 16 + 8 * (n & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(base + off0));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], 0u, 0u});
+}
+
+// Two C-layout MFMA results (4 rows each per lane) as one 8-slot bf16 operand.
+__device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b)
+{
+    const f32x8 x = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_convertvector(x, bf16x8);
+}
+
+}  // namespace tiles
+}  // namespace txl

@@ -61,6 +61,32 @@ hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t 
 // Key-range combine used by both kernels when nsplit > 1.
 hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s);
 
+// Backward of the relative attention (relattn_bwd_bf16.hip): bf16, dh = 64.
+struct RelAttnBwdArgs {
+    const void *q, *k, *v, *r, *out, *dout;
+    const float *u, *vb, *lse;
+    void *dq, *dk, *dv;
+    float *dr, *du, *dvb;
+    int64_t qs[3], ks[3], vs[3], os[3], rs[2];   // q/dq, k/dk, v/dv, out/dout (elements), r
+    int B, H, L, M, K;
+    float c;          // scale * log2(e)
+    float scale;
+    const int *mem_valid;
+    int window;
+    // workspace
+    uint16_t *qu, *qv;      // [B*H][L][64] bf16: c (q + u), c (q + vb)
+    float *dd, *lse2;       // [B*H][L]: rowsum(dout * out), lse * log2(e)
+    uint16_t *g;            // [B*H][L][kp] bf16: dS of (i, j) at column L-1-i+j
+    float *bias_part;       // [B*H][nqblk][2][64]: per 16-query block sums of dq's two parts
+    int kp;                 // row stride of g (K rounded up to 64)
+    int nqblk;              // 16-query blocks per head
+};
+
+size_t relattn_bwd_workspace_bytes(int B, int H, int L, int M);
+// Carves the workspace into a's workspace pointers (ws 256-byte aligned).
+void relattn_bwd_carve(RelAttnBwdArgs &a, void *ws);
+hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s);
+
 constexpr int kMaxMemBuffers = 64;
 
 struct MemUpdateArgs {

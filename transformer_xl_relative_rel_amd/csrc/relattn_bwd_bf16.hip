@@ -1,0 +1,671 @@
+// Relative-position attention, backward: bf16 in, fp32 accumulate, dh = 64,
+// for gfx950.
+//
+// The forward ([SRC] "Transformer-XL模型 核心源码阅读笔记",
+// RelPartialLearnableMultiHeadAttn.forward; [XL] "Transformer-XL" textbook
+// notes, "Relative Positional Encoding" and "Causal Mask With Memory") is
+//   s_ij = scale ((q_i + u) . k_j + (q_i + vb) . r[L-1-i+j]),
+//   visible iff lo(b, i) <= j <= i + M,   out_i = softmax_j(s_ij) . v_j.
+// The pages fix no backward; the gradients below are the chain rule on it
+// ([XL] "Why Stop Gradient" only detaches the memory states of a layer
+// stack: the attention still returns dk, dv for the memory keys, which a
+// layer needs for its projection weights).  With dP_ij = dout_i . v_j,
+// D_i = dout_i . out_i = sum_j p_ij dP_ij and dS_ij = p_ij (dP_ij - D_i):
+//   dq_i = scale sum_j dS_ij (k_j + r[L-1-i+j])
+//   dk_j = scale sum_i dS_ij (q_i + u),   dv_j = sum_i p_ij dout_i
+//   dr_c = scale sum over b and (i, j) with L-1-i+j = c of dS_ij (q_i + vb)
+//   du = sum over b, i of the k part of dq_i, dvb = the same of its r part.
+//
+// Kernels (one stream, in order):
+//   prep : c (q + u) and c (q + vb) rounded to bf16 exactly as the forward
+//          forms its query operands (c = scale log2 e), D_i, lse in log2 units.
+//   dq   : one wave per 16 queries, 8 waves per workgroup, keys in tiles of
+//          64, transposed like the forward (keys on MFMA rows, queries on
+//          lanes).  Recomputes p from lse (band MFMA + LDS skew rows + content
+//          MFMA, as the forward), dP^T = V . dout^T, dS; then
+//          dq^T += K^T . dS^T (K^T through the transposing LDS read) and, for
+//          the position part, writes dS into the skew row at key positions and
+//          reads it back at band positions: dq^T += R_band^T . G^T with
+//          G[i][c] = dS[i][c - (L-1-i)].  G is also stored to the workspace
+//          (row i, column c) for dr, and per-block sums of both dq parts go
+//          to the workspace for du and dvb.
+//   dkv  : one workgroup per 64 keys (4 waves of 16 keys), queries in steps of
+//          32, untransposed (queries on MFMA rows, keys on lanes).  The band
+//          T = c (q + vb) . R^T of the step's 32 queries and the 96 r rows
+//          they need is shared by the workgroup through LDS; each wave reads
+//          its skewed part, recomputes p and dS and accumulates
+//          dv^T += dout^T . P and dk^T += (c (q + u))^T . dS (operands of
+//          the step's query tiles through the transposing LDS read; P and dS
+//          pass from the score MFMA's result layout to the operand layout
+//          without data movement).
+//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r).
+//   bias : du, dvb from the per-block sums, in a fixed order.
+// No atomics: every output element has one writer and a fixed summation
+// order, so results are bitwise reproducible.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bf16_tiles.h"
+#include "internal.h"
+
+namespace txl {
+namespace {
+
+using namespace tiles;
+
+constexpr int BK = 64;           // keys per tile
+constexpr int NT = BK / 16;      // 16-key sub-tiles per tile
+constexpr int NBT = NT + 1;      // band tiles per 16-query block (79 rows)
+constexpr int NKK = DH / 32;     // MFMA k-steps over dh
+constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
+constexpr int TILE_CH = BK * CPR;
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// ---------------------------------------------------------------------------
+// prep: 32 rows per 256-thread workgroup, 8 threads (16 bytes each) per row.
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
+{
+    const int t = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * 32 + (t >> 3);
+    const int part = t & 7;
+    const int64_t nrows = (int64_t)a.B * a.H * a.L;
+    const bool ok = row < nrows;
+    const int64_t rr = ok ? row : 0;
+    const int bh = (int)(rr / a.L), i = (int)(rr - (int64_t)bh * a.L);
+    const int b = bh / a.H, h = bh - b * a.H;
+    float dsum = 0.f;
+    if (ok) {
+        const uint16_t *qp = static_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1] + (int64_t)i * a.qs[2];
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(qp + 8 * part);
+        const float *up = a.u + h * DH + 8 * part, *wp = a.vb + h * DH + 8 * part;
+        f32x8 fu, fv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = bf16_val((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            fu[e] = (x + up[e]) * a.c;     // same operation order as the forward's query operands
+            fv[e] = (x + wp[e]) * a.c;
+        }
+        *reinterpret_cast<bf16x8 *>(a.qu + rr * DH + 8 * part) = __builtin_convertvector(fu, bf16x8);
+        *reinterpret_cast<bf16x8 *>(a.qv + rr * DH + 8 * part) = __builtin_convertvector(fv, bf16x8);
+        const int64_t ooff = b * a.os[0] + h * a.os[1] + (int64_t)i * a.os[2] + 8 * part;
+        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.out) + ooff);
+        const u32x4 d = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.dout) + ooff);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            dsum += bf16_val((o[e >> 1] >> (16 * (e & 1))) & 0xffffu) * bf16_val((d[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    }
+    dsum += __shfl_xor(dsum, 1);
+    dsum += __shfl_xor(dsum, 2);
+    dsum += __shfl_xor(dsum, 4);
+    if (ok && part == 0) {
+        a.dd[rr] = dsum;
+        a.lse2[rr] = a.lse[rr] * LOG2E;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq (and G, and the bias partial sums)
+
+constexpr int QW = 8;               // waves per workgroup
+constexpr int QROWS = 16 * QW;      // queries per workgroup
+constexpr int QTHR = 64 * QW;
+constexpr int RQ = 4;               // r ring quarters: three in use, one loading
+static_assert(TILE_CH == QTHR, "one 16-byte load per thread per tile");
+static_assert(QROWS - 16 + 16 * NBT <= 64 * (RQ - 1), "a tile's bands fit in three ring quarters");
+
+// Skew row of query n (as the forward): written at columns 1..95, rows far
+// enough apart that one row's used columns never meet another's.
+__device__ __forceinline__ int skew_row(int n) { return 80 * n + 12 * (n >> 2); }
+constexpr int SKEW = 80 * 15 + 12 * 3 + 96;
+
+__global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sr[RQ][TILE_CH];
+    __shared__ __attribute__((aligned(16))) float sskew[QW][SKEW];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int BH = a.B * a.H, L = a.L, M = a.M, K = a.K;
+    const int nqb = (L + QROWS - 1) / QROWS;
+    const int wg = blockIdx.x;
+    const int qblk = nqb - 1 - wg / BH;            // the longest query blocks first
+    const int bh = wg - (wg / BH) * BH;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int i0 = QROWS * qblk;
+    const int i0w = i0 + 16 * wave;
+    const int iq = i0w + n;
+    const bool qok = iq < L;
+    const int ntile = (min(i0 + QROWS - 1, L - 1) + M) / BK + 1;
+    const int ntile_w = i0w < L ? (min(i0w + 15, L - 1) + M) / BK + 1 : 0;
+
+    // per-lane query operands and row constants
+    const int iqc = qok ? iq : 0;
+    const bf16x8 zero8 = {};
+    bf16x8 qu[NKK], qv[NKK], dof[NKK];
+    {
+        const uint16_t *qur = a.qu + ((int64_t)bh * L + iqc) * DH;
+        const uint16_t *qvr = a.qv + ((int64_t)bh * L + iqc) * DH;
+        const uint16_t *dor = static_cast<const uint16_t *>(a.dout) + b * a.os[0] + h * a.os[1] + (int64_t)iqc * a.os[2];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qur + 32 * kk + 8 * g);
+            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(qvr + 32 * kk + 8 * g);
+            const bf16x8 z = *reinterpret_cast<const bf16x8 *>(dor + 32 * kk + 8 * g);
+            qu[kk] = qok ? x : zero8;
+            qv[kk] = qok ? y : zero8;
+            dof[kk] = qok ? z : zero8;
+        }
+    }
+    const float nlse = qok ? -a.lse2[(int64_t)bh * L + iq] : -INFINITY;
+    const float nD = qok ? -a.dd[(int64_t)bh * L + iq] : 0.f;
+    int kmem_abs = 0;
+    if (a.mem_valid) {
+        int mv = a.mem_valid[b];
+        mv = mv < 0 ? 0 : (mv > M ? M : mv);
+        kmem_abs = M - mv;
+    }
+    const int win = a.window;
+
+    // direct loads: thread tid moves chunk tid of each 64-row tile
+    const int lrow = tid / CPR;
+    const int lch = ((tid & (CPR - 1)) ^ swz(lrow)) * 16;
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + b * a.vs[0] + h * a.vs[1];
+    const uint16_t *rp = static_cast<const uint16_t *>(a.r) + h * a.rs[0];
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
+    const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
+    const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
+    const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][wave * 64]));
+    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][wave * 64]));
+    const uint32_t sr_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0][wave * 64]));
+    // ring row x holds r row cb + x; wave w's band tile bt of key tile kt starts at
+    // ring row xw + 64 kt + 16 bt (band row cc of query n <-> key cc + n - 15)
+    const int cb = L - QROWS - i0;
+    const int xw = QROWS - 16 - 16 * wave;
+    auto load_kv = [&](int kt) {
+        const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
+        const int row = kt * BK + lrow;
+        load_lds16(krs, (uint32_t)(row * krow_b + lch), sk_base + boff);
+        load_lds16(vrs, (uint32_t)(row * vrow_b + lch), sv_base + boff);
+    };
+    auto load_r_quarter = [&](int q) {
+        const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
+        load_lds16(rrs, (uint32_t)((cb + 64 * q + lrow) * rrow_b + lch), sr_base + qoff);
+    };
+
+    f32x4 dqu[NDT], dqv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dqu[dt] = dqv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_kv(0);
+#pragma unroll
+    for (int q = 0; q < RQ - 1; ++q) load_r_quarter(q);
+    float *skw = sskew[wave];
+    const int rowb = skew_row(n);
+    uint16_t *grow = a.g + ((int64_t)bh * L + iqc) * a.kp;
+
+    for (int kt = 0; kt < ntile; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < ntile) {
+            load_kv(kt + 1);
+            load_r_quarter(kt + RQ - 1);
+        }
+        if (kt >= ntile_w) continue;
+        const int j0 = kt * BK;
+        const u32x4 *tk = sk[kt & 1], *tv = sv[kt & 1];
+
+        // band: T^T = R_band . (c (q + vb))^T - lse2, masked band rows at -inf
+        const int thi = M + i0w - j0 + 15;
+        const int tlo = win > 0 ? M + 1 - win + i0w - j0 + 15 : -(1 << 30);
+        f32x4 acc[NBT];
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) {
+            const int x0 = xw + 64 * kt + 16 * bt;   // wave-uniform, multiple of 16
+            const u32x4 *rq = sr[(x0 >> 6) & (RQ - 1)];
+            const int rr = (x0 & 63) + n;
+            f32x4 cin;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * bt + 4 * g + v;
+                cin[v] = (row > thi || row < tlo) ? -INFINITY : nlse;
+            }
+            acc[bt] = mfma(row_frag(rq, rr, 0, g), qv[0], cin);
+            acc[bt] = mfma(row_frag(rq, rr, 1, g), qv[1], acc[bt]);
+        }
+        lds_order();
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) {
+            float *dst = skw + rowb + 16 * bt + 4 * g + n + 1;
+            dst[0] = acc[bt][0];
+            dst[1] = acc[bt][1];
+            dst[2] = acc[bt][2];
+            dst[3] = acc[bt][3];
+        }
+        lds_order();
+        // content on top of the skewed band: log2-domain score minus lse
+        f32x4 sc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 cin = *reinterpret_cast<const f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (j0 + 16 * tt + 4 * g + v < kmem_abs) cin[v] = -INFINITY;
+            sc[tt] = cin;
+        }
+        lds_order();
+        f32x4 gs[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 s = mfma(row_frag(tk, 16 * tt + n, 0, g), qu[0], sc[tt]);
+            s = mfma(row_frag(tk, 16 * tt + n, 1, g), qu[1], s);
+            f32x4 dp = {nD, nD, nD, nD};
+            dp = mfma(row_frag(tv, 16 * tt + n, 0, g), dof[0], dp);
+            dp = mfma(row_frag(tv, 16 * tt + n, 1, g), dof[1], dp);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) gs[tt][v] = __builtin_amdgcn_exp2f(s[v]) * dp[v];
+        }
+        // content part of dq: dq^T += K^T . dS^T
+#pragma unroll
+        for (int ch = 0; ch < NT / 2; ++ch) {
+            const bf16x8 gf = pack8(gs[2 * ch], gs[2 * ch + 1]);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) dqu[dt] = mfma(col_frag(tk, 32 * ch, dt, g, n), gf, dqu[dt]);
+        }
+        // dS into the skew row at key positions, read back at band positions
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g) = gs[tt];
+        lds_order();
+        // position part: dq^T += R_band^T . G^T over band rows 0..79 in three
+        // k-steps (band rows 32 ks + {4g + e, 16 + 4g + e}; rows >= 80 are zero)
+        auto ring_tr = [&](int cc, int dt) -> u32x2 {
+            const int x = xw + 64 * kt + cc;
+            const u32x4 *rq = sr[(x >> 6) & (RQ - 1)];
+            const int r = x & 63;
+            TXL_LDS_AS char *base = (TXL_LDS_AS char *)(TXL_LDS_AS void *)rq;
+            const int chunk = 2 * dt + ((n >> 1) & 1);
+            const int off = (r * CPR + (chunk ^ swz(r))) * 16 + 8 * (n & 1);
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(base + off)));
+        };
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+            f32x8 gv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int cc = 32 * ks + 4 * g + e;
+                const int jj = cc + n - 15;
+                const float x = skw[rowb + cc + n + 1];
+                gv[e] = (jj >= 0 && jj < BK) ? x : 0.f;
+                if (ks < 2) {
+                    const float y = skw[rowb + cc + 16 + n + 1];
+                    gv[4 + e] = (jj + 16 >= 0 && jj + 16 < BK) ? y : 0.f;
+                } else {
+                    gv[4 + e] = 0.f;
+                }
+            }
+            const bf16x8 gt = __builtin_convertvector(gv, bf16x8);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const u32x2 lo = ring_tr(32 * ks + 4 * g + (n >> 2), dt);
+                const u32x2 hi = ks < 2 ? ring_tr(32 * ks + 16 + 4 * g + (n >> 2), dt) : u32x2{0u, 0u};
+                const bf16x8 rt = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                dqv[dt] = mfma(rt, gt, dqv[dt]);
+            }
+        }
+        lds_order();
+        // G row of this query: column L-1-i+j for the visible keys j of the tile
+        if (qok) {
+            const int pb = L - 1 - iq + j0 + 4 * g;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int p = pb + 16 * tt + v;
+                    if (p < K) grow[p] = bf16_bits(gs[tt][v]);
+                }
+        }
+    }
+
+    const float scale = a.scale;
+    if (qok) {
+        uint16_t *dqp = static_cast<uint16_t *>(a.dq) + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x4 y = __builtin_convertvector((dqu[dt] + dqv[dt]) * scale, bf16x4);
+            *reinterpret_cast<u32x2 *>(dqp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, y);
+        }
+    }
+    if (i0w < L) {
+        // sums over the 16 queries of this wave (queries past L contribute 0)
+        float *part = a.bias_part + ((int64_t)bh * a.nqblk + i0w / 16) * (2 * DH);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float su = dqu[dt][v] * scale, sw = dqv[dt][v] * scale;
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    su += __shfl_xor(su, o);
+                    sw += __shfl_xor(sw, o);
+                }
+                if (n == 0) {
+                    part[16 * dt + 4 * g + v] = su;
+                    part[DH + 16 * dt + 4 * g + v] = sw;
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv
+
+constexpr int KW = 4;               // waves per workgroup (16 keys each)
+constexpr int QS = 32;              // queries per step
+constexpr int QT_CH = QS * CPR;     // chunks per query tile
+constexpr int TS = 100;             // band row stride in floats (96 used)
+constexpr int KTHR = 64 * KW;
+static_assert(QT_CH == KTHR, "one 16-byte load per thread per query tile");
+
+__global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) u32x4 squ[2][QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sqv[2][QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sdo[2][QT_CH];
+    __shared__ __attribute__((aligned(16))) float sl2[2][QS];
+    __shared__ __attribute__((aligned(16))) float sdd[2][QS];
+    __shared__ __attribute__((aligned(16))) float tband[QS * TS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int BH = a.B * a.H, L = a.L, M = a.M, K = a.K;
+    const int wg = blockIdx.x;
+    const int kb = wg / BH;                      // the key blocks seen by most queries first
+    const int bh = wg - kb * BH;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int j0 = BK * kb;
+    const int jw = j0 + 16 * wave + n;           // this lane's key
+    const bool jok = jw < K;
+    const int jc = jok ? jw : 0;
+
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + b * a.vs[0] + h * a.vs[1];
+    const bf16x8 zero8 = {};
+    bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kp + (int64_t)jc * a.ks[2] + 32 * kk + 8 * g);
+        const bf16x8 y = *reinterpret_cast<const bf16x8 *>(vp + (int64_t)jc * a.vs[2] + 32 * kk + 8 * g);
+        kf[kk] = jok ? x : zero8;
+        vf[kk] = jok ? y : zero8;
+    }
+    int kmem_abs = 0;
+    if (a.mem_valid) {
+        int mv = a.mem_valid[b];
+        mv = mv < 0 ? 0 : (mv > M ? M : mv);
+        kmem_abs = M - mv;
+    }
+    const int win = a.window;
+    // queries below j0 - M see no key of the block; a block entirely below the
+    // valid memory is seen by nobody
+    int ibeg = j0 - M > 0 ? ((j0 - M) / QS) * QS : 0;
+    if (kmem_abs >= j0 + BK) ibeg = L;
+    const int nsteps = ibeg < L ? (L - ibeg + QS - 1) / QS : 0;
+
+    // loads of a query step: thread tid moves chunk tid of each 32-row tile
+    const int lrow = tid / CPR;
+    const int lch = ((tid & (CPR - 1)) ^ swz(lrow)) * 16;
+    const __amdgpu_buffer_rsrc_t qurs = make_rsrc(a.qu + (int64_t)bh * L * DH, (uint32_t)L * DH * 2);
+    const __amdgpu_buffer_rsrc_t qvrs = make_rsrc(a.qv + (int64_t)bh * L * DH, (uint32_t)L * DH * 2);
+    const uint16_t *dop = static_cast<const uint16_t *>(a.dout) + b * a.os[0] + h * a.os[1];
+    const __amdgpu_buffer_rsrc_t dors = make_rsrc(dop, (uint32_t)(((int64_t)(L - 1) * a.os[2] + DH) * 2));
+    const __amdgpu_buffer_rsrc_t l2rs = make_rsrc(a.lse2 + (int64_t)bh * L, (uint32_t)L * 4);
+    const __amdgpu_buffer_rsrc_t ddrs = make_rsrc(a.dd + (int64_t)bh * L, (uint32_t)L * 4);
+    const int dorow_b = (int)a.os[2] * 2;
+    const uint32_t squ_base = __builtin_amdgcn_readfirstlane(lds_addr(&squ[0][wave * 64]));
+    const uint32_t sqv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sqv[0][wave * 64]));
+    const uint32_t sdo_base = __builtin_amdgcn_readfirstlane(lds_addr(&sdo[0][wave * 64]));
+    const uint32_t sl2_base = __builtin_amdgcn_readfirstlane(lds_addr(&sl2[0][0]));
+    const uint32_t sdd_base = __builtin_amdgcn_readfirstlane(lds_addr(&sdd[0][0]));
+    auto issue = [&](int s) {
+        const int i0 = ibeg + QS * s;
+        const uint32_t boff = (uint32_t)(s & 1) * (QT_CH * 16);
+        const int row = i0 + lrow;
+        load_lds16(qurs, (uint32_t)(row * DH * 2 + lch), squ_base + boff);
+        load_lds16(qvrs, (uint32_t)(row * DH * 2 + lch), sqv_base + boff);
+        load_lds16(dors, (uint32_t)(row * dorow_b + lch), sdo_base + boff);
+        // lse2 and D of the 32 queries: 8 lanes of 16 bytes each
+        if (wave == 0 && lane < QS / 4) load_lds16(l2rs, (uint32_t)((i0 + 4 * lane) * 4), sl2_base + (uint32_t)(s & 1) * (QS * 4));
+        if (wave == 1 && lane < QS / 4) load_lds16(ddrs, (uint32_t)((i0 + 4 * lane) * 4), sdd_base + (uint32_t)(s & 1) * (QS * 4));
+    };
+
+    const uint16_t *rp = static_cast<const uint16_t *>(a.r) + h * a.rs[0];
+    const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
+    const int rrow_b = (int)a.rs[1] * 2;
+
+    f32x4 dkt[NDT], dvt[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dkt[dt] = dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nsteps > 0) issue(0);
+    // band tiles of this wave: query rows 16 s2 .. +15, band columns 16 pt .. +15
+    const int s2 = wave & 1;
+    const int pt0 = 3 * (wave >> 1);
+    for (int s = 0; s < nsteps; ++s) {
+        const int i0 = ibeg + QS * s;
+        const int buf = s & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (s + 1 < nsteps) issue(s + 1);
+        // T[i][c] = c (q_i + vb) . r[pw + c] - lse2_i for the step's queries,
+        // with pw the r row of (last query, first key); masked entries -inf
+        const int pw = L - 1 - (i0 + QS - 1) + j0;
+        {
+            const bf16x8 qa0 = row_frag(sqv[buf], 16 * s2 + n, 0, g);
+            const bf16x8 qa1 = row_frag(sqv[buf], 16 * s2 + n, 1, g);
+            f32x4 nl;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * s2 + 4 * g + v;
+                nl[v] = (i0 + r < L) ? -sl2[buf][r] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int pc = pw + 16 * (pt0 + u) + n;     // this lane's r row
+                const bf16x8 rb0 = load16(rrs, (uint32_t)(pc * rrow_b + 8 * g * 2));
+                const bf16x8 rb1 = load16(rrs, (uint32_t)(pc * rrow_b + (32 + 8 * g) * 2));
+                const bool cm = pc > K - 1 || (win > 0 && pc < K - win);
+                f32x4 cin;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cin[v] = cm ? -INFINITY : nl[v];
+                f32x4 acc = mfma(qa0, rb0, cin);
+                acc = mfma(qa1, rb1, acc);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[v];
+            }
+        }
+        __syncthreads();
+        // scores, probabilities and dS of this wave's 16 keys
+        f32x4 p[2], gs[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            f32x4 cin;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * x + 4 * g + v;
+                cin[v] = tband[r * TS + 16 * wave + n - r + QS - 1];
+                if (jw < kmem_abs) cin[v] = -INFINITY;
+            }
+            f32x4 sc = mfma(row_frag(squ[buf], 16 * x + n, 0, g), kf[0], cin);
+            sc = mfma(row_frag(squ[buf], 16 * x + n, 1, g), kf[1], sc);
+            f32x4 dp;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dp[v] = -sdd[buf][16 * x + 4 * g + v];
+            dp = mfma(row_frag(sdo[buf], 16 * x + n, 0, g), vf[0], dp);
+            dp = mfma(row_frag(sdo[buf], 16 * x + n, 1, g), vf[1], dp);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                p[x][v] = __builtin_amdgcn_exp2f(sc[v]);
+                gs[x][v] = p[x][v] * dp[v];
+            }
+        }
+        const bf16x8 pb = pack8(p[0], p[1]);
+        const bf16x8 gb = pack8(gs[0], gs[1]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            dvt[dt] = mfma(col_frag(sdo[buf], 0, dt, g, n), pb, dvt[dt]);
+            dkt[dt] = mfma(col_frag(squ[buf], 0, dt, g, n), gb, dkt[dt]);
+        }
+    }
+
+    if (jok) {
+        uint16_t *dkp = static_cast<uint16_t *>(a.dk) + b * a.ks[0] + h * a.ks[1] + (int64_t)jw * a.ks[2];
+        uint16_t *dvp = static_cast<uint16_t *>(a.dv) + b * a.vs[0] + h * a.vs[1] + (int64_t)jw * a.vs[2];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            // dk = scale sum dS (q + u) = (scale / c) sum dS c (q + u) = ln 2 sum dS qu
+            const bf16x4 yk = __builtin_convertvector(dkt[dt] * LN2, bf16x4);
+            const bf16x4 yv = __builtin_convertvector(dvt[dt], bf16x4);
+            *reinterpret_cast<u32x2 *>(dkp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yk);
+            *reinterpret_cast<u32x2 *>(dvp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dr: one workgroup per 64 rows of r; 4 waves of 16 rows; queries of every
+// batch row in steps of 32.
+
+constexpr int RW = 4;
+
+__global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) u32x4 sg[QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sq[QT_CH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int L = a.L, K = a.K;
+    const int nkb = (K + BK - 1) / BK;
+    const int h = blockIdx.x / nkb;
+    const int p0 = BK * (blockIdx.x - h * nkb);
+    const int lrow = tid / CPR, lpos = tid & (CPR - 1);
+    const int lc = lpos ^ swz(lrow);              // chunk this thread moves
+    // rows i with a column >= L-1-i in [p0, p0 + 63]
+    const int ilo = L - 1 - (p0 + BK - 1) > 0 ? ((L - 1 - (p0 + BK - 1)) / QS) * QS : 0;
+
+    f32x4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < a.B; ++b) {
+        const int64_t bh = (int64_t)b * a.H + h;
+        for (int i0 = ilo; i0 < L; i0 += QS) {
+            const int i = i0 + lrow;
+            u32x4 gr = {0u, 0u, 0u, 0u}, qr = {0u, 0u, 0u, 0u};
+            if (i < L) {
+                gr = *reinterpret_cast<const u32x4 *>(a.g + (bh * L + i) * a.kp + p0 + 8 * lc);
+                qr = *reinterpret_cast<const u32x4 *>(a.qv + (bh * L + i) * DH + 8 * lc);
+                // columns below L-1-i (keys before the first) and at or past K were never written
+                const int cmin = L - 1 - i;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int col = p0 + 8 * lc + e;
+                    if (col < cmin || col >= K) gr[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                }
+            }
+            __syncthreads();
+            sg[lrow * CPR + lpos] = gr;
+            sq[lrow * CPR + lpos] = qr;
+            __syncthreads();
+            const bf16x8 ga = col_frag(sg, 0, wave, g, n);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag(sq, 0, dt, g, n), acc[dt]);
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int p = p0 + 16 * wave + 4 * g + v;
+            // dr = scale sum dS (q + vb) = ln 2 sum dS c (q + vb)
+            if (p < K) a.dr[((int64_t)h * K + p) * DH + 16 * dt + n] = acc[dt][v] * LN2;
+        }
+}
+
+// du, dvb: sums of the per-block partial sums in (b, block) order.
+__global__ __launch_bounds__(2 * DH) void bwd_bias_kernel(RelAttnBwdArgs a)
+{
+    const int h = blockIdx.x, t = threadIdx.x;
+    const int which = t / DH, d = t - which * DH;
+    float s = 0.f;
+    for (int b = 0; b < a.B; ++b) {
+        const float *pp = a.bias_part + ((int64_t)(b * a.H + h) * a.nqblk) * (2 * DH) + which * DH + d;
+        for (int k = 0; k < a.nqblk; ++k) s += pp[(int64_t)k * 2 * DH];
+    }
+    (which ? a.dvb : a.du)[h * DH + d] = s;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+    size_t qu, qv, dd, lse2, part, g, total;
+};
+
+BwdLayout bwd_layout(int B, int H, int L, int M)
+{
+    const size_t rows = (size_t)B * H * L;
+    const int K = M + L;
+    const size_t kp = (size_t)((K + BK - 1) / BK) * BK;
+    const size_t nqblk = (size_t)(L + 15) / 16;
+    BwdLayout l{};
+    size_t off = 0;
+    l.qu = off; off += round256(rows * DH * 2);
+    l.qv = off; off += round256(rows * DH * 2);
+    l.dd = off; off += round256(rows * 4);
+    l.lse2 = off; off += round256(rows * 4);
+    l.part = off; off += round256((size_t)B * H * nqblk * 2 * DH * 4);
+    l.g = off; off += round256(rows * kp * 2);
+    l.total = off;
+    return l;
+}
+
+}  // namespace
+
+size_t relattn_bwd_workspace_bytes(int B, int H, int L, int M) { return bwd_layout(B, H, L, M).total; }
+
+void relattn_bwd_carve(RelAttnBwdArgs &a, void *ws)
+{
+    const BwdLayout l = bwd_layout(a.B, a.H, a.L, a.M);
+    char *base = static_cast<char *>(ws);
+    a.qu = reinterpret_cast<uint16_t *>(base + l.qu);
+    a.qv = reinterpret_cast<uint16_t *>(base + l.qv);
+    a.dd = reinterpret_cast<float *>(base + l.dd);
+    a.lse2 = reinterpret_cast<float *>(base + l.lse2);
+    a.bias_part = reinterpret_cast<float *>(base + l.part);
+    a.g = reinterpret_cast<uint16_t *>(base + l.g);
+    a.kp = ((a.K + BK - 1) / BK) * BK;
+    a.nqblk = (a.L + 15) / 16;
+}
+
+hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
+{
+    const int64_t rows = (int64_t)a.B * a.H * a.L;
+    const int BH = a.B * a.H;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS))), dim3(QTHR), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + BK - 1) / BK))), dim3(KTHR), 0, s, a);
+    hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
+    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)a.H), dim3(2 * DH), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace txl

@@ -261,6 +261,90 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     return ok();
 }
 
+// The backward kernels support bf16 with dh = 64 and address one head's rows
+// with 32-bit byte offsets.
+static txl_status check_bwd(const txl_relattn_desc *d)
+{
+    txl_status s = check_desc(d);
+    if (s != TXL_OK) return s;
+    if (d->dtype != TXL_BF16 || d->dh != 64)
+        return fail(TXL_ERR_UNSUPPORTED, "the backward supports bf16 with dh = 64 (got %s, dh=%d)",
+                    d->dtype == TXL_BF16 ? "bf16" : "f32", d->dh);
+    const int64_t K = (int64_t)d->L + d->M;
+    const int64_t row = std::max(std::max(d->k_stride[2], d->v_stride[2]), d->r_stride[1]);
+    if ((K + 64) * row * 2 >= ((int64_t)1 << 31) || ((int64_t)d->L + 32) * d->o_stride[2] * 2 >= ((int64_t)1 << 31))
+        return fail(TXL_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
+    return TXL_OK;
+}
+
+txl_status txl_relattn_bwd_workspace_size(const txl_relattn_desc *d, size_t *bytes)
+{
+    txl_status s = check_bwd(d);
+    if (s != TXL_OK) return s;
+    if (!bytes) return fail(TXL_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = txl::relattn_bwd_workspace_bytes(d->B, d->H, d->L, d->M);
+    return ok();
+}
+
+txl_status txl_relattn_bwd(const txl_relattn_desc *d, const void *q, const void *k, const void *v, const void *r_k,
+                           const float *u, const float *vb, const void *out, const float *lse, const void *dout,
+                           void *dq, void *dk, void *dv, float *dr, float *du, float *dvb, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    txl_status s = check_bwd(d);
+    if (s != TXL_OK) return s;
+    if (!q || !k || !v || !r_k || !u || !vb || !out || !lse || !dout || !dq || !dk || !dv || !dr || !du || !dvb)
+        return fail(TXL_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void *a16[] = {q, k, v, r_k, out, dout, dq, dk, dv, dr};
+    for (const void *p : a16)
+        if (!aligned16(p)) return fail(TXL_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(vb) | reinterpret_cast<uintptr_t>(lse) |
+         reinterpret_cast<uintptr_t>(du) | reinterpret_cast<uintptr_t>(dvb)) & 3u)
+        return fail(TXL_ERR_INVALID_ARG, "u, vb, lse, du and dvb must be 4-byte aligned");
+    const size_t need = txl::relattn_bwd_workspace_bytes(d->B, d->H, d->L, d->M);
+    if (!workspace || workspace_bytes < need)
+        return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(TXL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const int K = d->M + d->L;
+    const int cq[3] = {d->B, d->H, d->L}, ck[3] = {d->B, d->H, K}, cr[2] = {d->H, K};
+    const uintptr_t hd = (uintptr_t)d->H * d->dh * sizeof(float);
+    auto flat = [](const void *p, size_t bytes) {
+        return Extent{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + bytes};
+    };
+    const Extent ins[9] = {extent(q, d->q_stride, cq, 3, d->dh, 2), extent(k, d->k_stride, ck, 3, d->dh, 2),
+                           extent(v, d->v_stride, ck, 3, d->dh, 2), extent(r_k, d->r_stride, cr, 2, d->dh, 2),
+                           extent(out, d->o_stride, cq, 3, d->dh, 2), extent(dout, d->o_stride, cq, 3, d->dh, 2),
+                           flat(lse, (size_t)d->B * d->H * d->L * sizeof(float)), flat(u, hd), flat(vb, hd)};
+    const Extent outs[7] = {extent(dq, d->q_stride, cq, 3, d->dh, 2), extent(dk, d->k_stride, ck, 3, d->dh, 2),
+                            extent(dv, d->v_stride, ck, 3, d->dh, 2),
+                            flat(dr, (size_t)d->H * K * d->dh * sizeof(float)), flat(du, hd), flat(dvb, hd),
+                            flat(workspace, need)};
+    for (int o = 0; o < 7; ++o) {
+        for (const Extent &e : ins)
+            if (overlap(outs[o], e)) return fail(TXL_ERR_ALIAS, "an output or the workspace overlaps an input");
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlap(outs[o], outs[o2])) return fail(TXL_ERR_ALIAS, "two outputs (or the workspace) overlap");
+    }
+    txl::RelAttnBwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.r = r_k; a.out = out; a.dout = dout;
+    a.u = u; a.vb = vb; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dr = dr; a.du = du; a.dvb = dvb;
+    for (int t = 0; t < 3; ++t) {
+        a.qs[t] = d->q_stride[t]; a.ks[t] = d->k_stride[t]; a.vs[t] = d->v_stride[t]; a.os[t] = d->o_stride[t];
+    }
+    a.rs[0] = d->r_stride[0]; a.rs[1] = d->r_stride[1];
+    a.B = d->B; a.H = d->H; a.L = d->L; a.M = d->M; a.K = K;
+    a.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dh);
+    a.c = (float)((double)a.scale * 1.4426950408889634);
+    a.mem_valid = d->mem_valid;
+    a.window = d->window;
+    txl::relattn_bwd_carve(a, workspace);
+    hipError_t e = txl::launch_relattn_bwd_bf16(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur, const void *const *h, int L,
                                     void *const *new_mem, int mem_len, int ext_len, int B, int d, int dtype,
                                     int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new, void *stream)

@@ -77,7 +77,7 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 # Fixed stream numbers, one per tensor role, so every consumer draws the same values.
-STREAM = {"q": 1, "k": 2, "v": 3, "r": 4, "u": 5, "vb": 6, "h": 7, "mem": 8, "w_r": 9, "emb": 10}
+STREAM = {"q": 1, "k": 2, "v": 3, "r": 4, "u": 5, "vb": 6, "h": 7, "mem": 8, "w_r": 9, "emb": 10, "dout": 11}
 
 
 def relattn_inputs(B: int, H: int, L: int, M: int, dh: int, dtype: str = "bf16",
