@@ -8,6 +8,12 @@ resident in HBM before timing starts.
 Prints one JSON line.  value = algorithmic TFLOP/s of the whole step:
 F_alg = 6 * dh * B * H * V with V = L*M + L*(L+1)/2 visible (query, key)
 pairs per head (three contractions over the visible pairs).
+
+The line also carries "backward": the gradients of the same attention call
+(txl_relattn_bwd on the forward's out and lse and a synthetic upstream
+gradient), timed over the same number of back-to-back calls, with
+F_bwd = 16 * dh * B * H * V (eight contractions over the visible pairs: the
+two score terms recomputed, dP, dv, dk, the two parts of dq, dr).
 """
 from __future__ import annotations
 
@@ -29,6 +35,11 @@ PEAK_HBM_GBS = 8000.0
 def flops_alg(B, H, L, M, dh):
     vis = L * M + L * (L + 1) // 2
     return 6.0 * dh * B * H * vis
+
+
+def flops_bwd(B, H, L, M, dh):
+    vis = L * M + L * (L + 1) // 2
+    return 16.0 * dh * B * H * vis
 
 
 def min_bytes(B, H, L, M, dh, es=2):
@@ -75,6 +86,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one Tail_M copy of this many MiB (bigger than every cache) so that a "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE pass can calibrate its counters against known bytes")
@@ -135,6 +147,32 @@ def main():
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / args.steps
+    bwd = None
+    if not args.no_backward:
+        dout = torch.from_numpy(synth.round_bf16(synth.normal((B, H, L, dh), synth.STREAM["dout"]))).to(dev).to(
+            torch.bfloat16)
+        out_b, lse_b = txl.relattn_fwd(q, k, v, r, u, vb, want_lse=True, stream=stream)
+        ws_b = torch.empty(txl.relattn_bwd_workspace_size(q, k, v, r, out_b, dout), dtype=torch.uint8, device=dev)
+        grads = txl.relattn_bwd(q, k, v, r, u, vb, out_b, lse_b, dout, workspace=ws_b, stream=stream)
+        gkw = dict(zip(("dq", "dk", "dv", "dr", "du", "dvb"), grads))
+
+        def backward():
+            txl.relattn_bwd(q, k, v, r, u, vb, out_b, lse_b, dout, workspace=ws_b, stream=stream, **gkw)
+
+        for _ in range(args.warmup):
+            backward()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.steps):
+            backward()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.steps
+        Fb = flops_bwd(B, H, L, M, dh)
+        bwd = {"ms_per_call": round(bwd_ms, 5), "tflops_alg": round(Fb / (bwd_ms * 1e-3) / 1e12, 2),
+               "pct_bf16_peak": round(100.0 * Fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+               "flops_per_call": Fb, "kernels": "prep, dq, dkv, dr, bias (txl_relattn_bwd)"}
     F = flops_alg(B, H, L, M, dh)
     value = F / (ms_step * 1e-3) / 1e12
     achieved = F / (attn_ms * 1e-3) / 1e12
@@ -152,6 +190,8 @@ def main():
                                                               "relattn_fwd_bf16.hip")),
                      "kernel": "relattn_fwd_bf16_kernel", "kernel_ms": round(attn_ms, 5)},
     }
+    if bwd is not None:
+        res["backward"] = bwd
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(d, B, H, L, M, dh)
     print(json.dumps(res), flush=True)

@@ -32,7 +32,8 @@
 //   dkv  : one workgroup per 64 keys (4 waves of 16 keys), queries in steps of
 //          32, untransposed (queries on MFMA rows, keys on lanes).  The band
 //          T = c (q + vb) . R^T of the step's 32 queries and the 96 r rows
-//          they need is shared by the workgroup through LDS; each wave reads
+//          they need (a ring of r rows in LDS, loaded a step ahead with the
+//          query tiles) is shared by the workgroup through LDS; each wave reads
 //          its skewed part, recomputes p and dS and accumulates
 //          dv^T += dout^T . P and dk^T += (c (q + u))^T . dS (operands of
 //          the step's query tiles through the transposing LDS read; P and dS
@@ -212,6 +213,21 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     const int rowb = skew_row(n);
     uint16_t *grow = a.g + ((int64_t)bh * L + iqc) * a.kp;
 
+    // The G row of a tile is stored at the start of the next iteration, right
+    // after that iteration's loads, so that the wait for the next tile's loads
+    // does not also wait for stores issued just before it.
+    f32x4 gprev[NT];
+    auto store_g = [&](int kt) {
+        if (!qok) return;
+        const int pb = L - 1 - iq + kt * BK + 4 * g;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int p = pb + 16 * tt + v;
+                if (p < K) grow[p] = bf16_bits(gprev[tt][v]);
+            }
+    };
     for (int kt = 0; kt < ntile; ++kt) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -219,6 +235,7 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
             load_kv(kt + 1);
             load_r_quarter(kt + RQ - 1);
         }
+        if (kt >= 1 && kt - 1 < ntile_w) store_g(kt - 1);
         if (kt >= ntile_w) continue;
         const int j0 = kt * BK;
         const u32x4 *tk = sk[kt & 1], *tv = sv[kt & 1];
@@ -321,18 +338,11 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
             }
         }
         lds_order();
-        // G row of this query: column L-1-i+j for the visible keys j of the tile
-        if (qok) {
-            const int pb = L - 1 - iq + j0 + 4 * g;
+        // G row of this query (column L-1-i+j for key j), stored next iteration
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int p = pb + 16 * tt + v;
-                    if (p < K) grow[p] = bf16_bits(gs[tt][v]);
-                }
-        }
+        for (int tt = 0; tt < NT; ++tt) gprev[tt] = gs[tt];
     }
+    if (ntile_w == ntile) store_g(ntile - 1);
 
     const float scale = a.scale;
     if (qok) {
@@ -370,7 +380,8 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 constexpr int KW = 4;               // waves per workgroup (16 keys each)
 constexpr int QS = 32;              // queries per step
 constexpr int QT_CH = QS * CPR;     // chunks per query tile
-constexpr int TS = 100;             // band row stride in floats (96 used)
+constexpr int TS = 97;              // band row stride in floats (96 used)
+constexpr int RSEG = 4;             // r ring segments of QS rows: three in use, one loading
 constexpr int KTHR = 64 * KW;
 static_assert(QT_CH == KTHR, "one 16-byte load per thread per query tile");
 
@@ -382,6 +393,7 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
     __shared__ __attribute__((aligned(16))) float sl2[2][QS];
     __shared__ __attribute__((aligned(16))) float sdd[2][QS];
     __shared__ __attribute__((aligned(16))) float tband[QS * TS];
+    __shared__ __attribute__((aligned(16))) u32x4 sring[RSEG][QT_CH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -447,15 +459,31 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         if (wave == 1 && lane < QS / 4) load_lds16(ddrs, (uint32_t)((i0 + 4 * lane) * 4), sdd_base + (uint32_t)(s & 1) * (QS * 4));
     };
 
+    // r rows of the band: step s needs rows pw_s .. pw_s + 95 with
+    // pw_s = L - QS - i0_s + j0, which moves down by QS per step.  Ring segment
+    // sg (slot sg % RSEG) holds rows pwl + QS sg .. + QS - 1, pwl being pw of
+    // the last step; step s uses segments nsteps-1-s .. nsteps+1-s and loads
+    // segment nsteps-2-s for the next step.  Rows outside [0, K) read zeros.
     const uint16_t *rp = static_cast<const uint16_t *>(a.r) + h * a.rs[0];
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
     const int rrow_b = (int)a.rs[1] * 2;
+    const int pwl = L - QS - (ibeg + QS * (nsteps - 1)) + j0;
+    const uint32_t sring_base = __builtin_amdgcn_readfirstlane(lds_addr(&sring[0][wave * 64]));
+    auto load_seg = [&](int sgm) {
+        load_lds16(rrs, (uint32_t)((pwl + QS * sgm + lrow) * rrow_b + lch),
+                   sring_base + (uint32_t)(sgm & (RSEG - 1)) * (QT_CH * 16));
+    };
 
     f32x4 dkt[NDT], dvt[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dkt[dt] = dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nsteps > 0) issue(0);
+    if (nsteps > 0) {
+        issue(0);
+        load_seg(nsteps - 1);
+        load_seg(nsteps);
+        load_seg(nsteps + 1);
+    }
     // band tiles of this wave: query rows 16 s2 .. +15, band columns 16 pt .. +15
     const int s2 = wave & 1;
     const int pt0 = 3 * (wave >> 1);
@@ -464,7 +492,10 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         const int buf = s & 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (s + 1 < nsteps) issue(s + 1);
+        if (s + 1 < nsteps) {
+            issue(s + 1);
+            load_seg(nsteps - 2 - s);
+        }
         // T[i][c] = c (q_i + vb) . r[pw + c] - lse2_i for the step's queries,
         // with pw the r row of (last query, first key); masked entries -inf
         const int pw = L - 1 - (i0 + QS - 1) + j0;
@@ -479,9 +510,11 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
             }
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
-                const int pc = pw + 16 * (pt0 + u) + n;     // this lane's r row
-                const bf16x8 rb0 = load16(rrs, (uint32_t)(pc * rrow_b + 8 * g * 2));
-                const bf16x8 rb1 = load16(rrs, (uint32_t)(pc * rrow_b + (32 + 8 * g) * 2));
+                const int pt = pt0 + u;
+                const int pc = pw + 16 * pt + n;            // this lane's r row
+                const u32x4 *seg = sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)];
+                const bf16x8 rb0 = row_frag(seg, 16 * (pt & 1) + n, 0, g);
+                const bf16x8 rb1 = row_frag(seg, 16 * (pt & 1) + n, 1, g);
                 const bool cm = pc > K - 1 || (win > 0 && pc < K - win);
                 f32x4 cin;
 #pragma unroll
@@ -541,77 +574,112 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dr: one workgroup per 64 rows of r; 4 waves of 16 rows; queries of every
-// batch row in steps of 32.
+// dr: one workgroup per 64 rows of r, 16 waves: wave w takes rows
+// 16 (w % 4) .. + 15 of the tile for the batch rows b = w / 4 (mod 4); the
+// four batch groups stage their own tiles, prefetched one step ahead in
+// registers, and their sums are added in group order at the end.
 
-constexpr int RW = 4;
+constexpr int RW = 16;
+constexpr int RG = 4;               // batch groups
 
 __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
 {
-    __shared__ __attribute__((aligned(16))) u32x4 sg[QT_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 sq[QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sg[RG][QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sq[RG][QT_CH];
+    __shared__ __attribute__((aligned(16))) f32x4 red[RG - 1][4 * NDT * 64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
+    const int psub = wave & 3, bg = wave >> 2;
     const int L = a.L, K = a.K;
     const int nkb = (K + BK - 1) / BK;
     const int h = blockIdx.x / nkb;
     const int p0 = BK * (blockIdx.x - h * nkb);
-    const int lrow = tid / CPR, lpos = tid & (CPR - 1);
+    const int tg = psub * 64 + lane;              // thread within the batch group
+    const int lrow = tg / CPR, lpos = tg & (CPR - 1);
     const int lc = lpos ^ swz(lrow);              // chunk this thread moves
     // rows i with a column >= L-1-i in [p0, p0 + 63]
     const int ilo = L - 1 - (p0 + BK - 1) > 0 ? ((L - 1 - (p0 + BK - 1)) / QS) * QS : 0;
+    const int nch = (L - ilo + QS - 1) / QS;
+    const int nsteps = ((a.B + RG - 1) / RG) * nch;   // same count for every group
+
+    auto fetch = [&](int t, u32x4 &gr, u32x4 &qr) {
+        const int b = bg + RG * (t / nch);
+        const int i = ilo + QS * (t % nch) + lrow;
+        gr = u32x4{0u, 0u, 0u, 0u};
+        qr = u32x4{0u, 0u, 0u, 0u};
+        if (b < a.B && i < L) {
+            const int64_t bh = (int64_t)b * a.H + h;
+            gr = *reinterpret_cast<const u32x4 *>(a.g + (bh * L + i) * a.kp + p0 + 8 * lc);
+            qr = *reinterpret_cast<const u32x4 *>(a.qv + (bh * L + i) * DH + 8 * lc);
+            // columns below L-1-i (keys before the first) and at or past K were never written
+            const int cmin = L - 1 - i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = p0 + 8 * lc + e;
+                if (col < cmin || col >= K) gr[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+        }
+    };
 
     f32x4 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < a.B; ++b) {
-        const int64_t bh = (int64_t)b * a.H + h;
-        for (int i0 = ilo; i0 < L; i0 += QS) {
-            const int i = i0 + lrow;
-            u32x4 gr = {0u, 0u, 0u, 0u}, qr = {0u, 0u, 0u, 0u};
-            if (i < L) {
-                gr = *reinterpret_cast<const u32x4 *>(a.g + (bh * L + i) * a.kp + p0 + 8 * lc);
-                qr = *reinterpret_cast<const u32x4 *>(a.qv + (bh * L + i) * DH + 8 * lc);
-                // columns below L-1-i (keys before the first) and at or past K were never written
-                const int cmin = L - 1 - i;
+    u32x4 gr, qr;
+    if (nsteps > 0) fetch(0, gr, qr);
+    for (int t = 0; t < nsteps; ++t) {
+        __syncthreads();
+        sg[bg][lrow * CPR + lpos] = gr;
+        sq[bg][lrow * CPR + lpos] = qr;
+        __syncthreads();
+        if (t + 1 < nsteps) fetch(t + 1, gr, qr);
+        const bf16x8 ga = col_frag(sg[bg], 0, psub, g, n);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int col = p0 + 8 * lc + e;
-                    if (col < cmin || col >= K) gr[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                }
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag(sq[bg], 0, dt, g, n), acc[dt]);
+    }
+    if (bg > 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) red[bg - 1][(psub * NDT + dt) * 64 + lane] = acc[dt];
+    }
+    __syncthreads();
+    if (bg == 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            f32x4 s = acc[dt];
+#pragma unroll
+            for (int k = 0; k < RG - 1; ++k) s += red[k][(psub * NDT + dt) * 64 + lane];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int p = p0 + 16 * psub + 4 * g + v;
+                // dr = scale sum dS (q + vb) = ln 2 sum dS c (q + vb)
+                if (p < K) a.dr[((int64_t)h * K + p) * DH + 16 * dt + n] = s[v] * LN2;
             }
-            __syncthreads();
-            sg[lrow * CPR + lpos] = gr;
-            sq[lrow * CPR + lpos] = qr;
-            __syncthreads();
-            const bf16x8 ga = col_frag(sg, 0, wave, g, n);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag(sq, 0, dt, g, n), acc[dt]);
         }
     }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int p = p0 + 16 * wave + 4 * g + v;
-            // dr = scale sum dS (q + vb) = ln 2 sum dS c (q + vb)
-            if (p < K) a.dr[((int64_t)h * K + p) * DH + 16 * dt + n] = acc[dt][v] * LN2;
-        }
 }
 
-// du, dvb: sums of the per-block partial sums in (b, block) order.
-__global__ __launch_bounds__(2 * DH) void bwd_bias_kernel(RelAttnBwdArgs a)
+// du, dvb: the per-block partial sums of one head, 16 waves each summing every
+// 16th (batch row, block) item, then the 16 wave sums in wave order.
+__global__ __launch_bounds__(1024) void bwd_bias_kernel(RelAttnBwdArgs a)
 {
-    const int h = blockIdx.x, t = threadIdx.x;
-    const int which = t / DH, d = t - which * DH;
+    __shared__ float red[16][DH];
+    const int h = blockIdx.x >> 1, which = blockIdx.x & 1;
+    const int t = threadIdx.x, wave = t >> 6, d = t & 63;
+    const int nitems = a.B * a.nqblk;
     float s = 0.f;
-    for (int b = 0; b < a.B; ++b) {
-        const float *pp = a.bias_part + ((int64_t)(b * a.H + h) * a.nqblk) * (2 * DH) + which * DH + d;
-        for (int k = 0; k < a.nqblk; ++k) s += pp[(int64_t)k * 2 * DH];
+#pragma unroll 4
+    for (int it = wave; it < nitems; it += 16) {
+        const int b = it / a.nqblk, k = it - b * a.nqblk;
+        s += a.bias_part[((int64_t)(b * a.H + h) * a.nqblk + k) * (2 * DH) + which * DH + d];
     }
-    (which ? a.dvb : a.du)[h * DH + d] = s;
+    red[wave][d] = s;
+    __syncthreads();
+    if (wave == 0) {
+        float tot = 0.f;
+        for (int w = 0; w < 16; ++w) tot += red[w][d];
+        (which ? a.dvb : a.du)[h * DH + d] = tot;
+    }
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -664,7 +732,7 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS))), dim3(QTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + BK - 1) / BK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
-    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)a.H), dim3(2 * DH), 0, s, a);
+    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
