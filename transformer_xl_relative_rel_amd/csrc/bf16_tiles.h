@@ -110,6 +110,49 @@ __device__ __forceinline__ bf16x8 col_frag_lo(const u32x4 *tile, int rb, int dt,
     return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], 0u, 0u});
 }
 
+// The same reads with the lane part of the address computed once.  For a
+// block of rows starting at a multiple of 16, swz(row) depends on the lane
+// only: ((16 k + 4 g + (n >> 2)) >> 1) & 7 = (2 g + (n >> 3)) & 7.
+//   row_lane_off: byte offset of lane (g, n)'s chunk (4 kk + g) in row n of
+//     the block -- row fragments;
+//   tr_lane_off: byte offset of lane (g, n)'s 8 bytes for output column
+//     block dt in rows 4 g + (n >> 2) of the block -- transposing reads.
+__device__ __forceinline__ int row_lane_off(int kk, int g, int n)
+{
+    return (n * CPR + ((4 * kk + g) ^ ((n >> 1) & (CPR - 1)))) * 16;
+}
+__device__ __forceinline__ int tr_lane_off(int dt, int g, int n)
+{
+    const int r = 4 * g + (n >> 2);
+    return (r * CPR + ((2 * dt + ((n >> 1) & 1)) ^ ((r >> 1) & (CPR - 1)))) * 16 + 8 * (n & 1);
+}
+// Row fragment of the 16-row block at byte `blk` (row16 * CPR * 16 bytes into
+// a tile, row16 a multiple of 16) with a precomputed row_lane_off.
+__device__ __forceinline__ bf16x8 row_frag_at(const TXL_LDS_AS char *blk, int lane_off)
+{
+    return *(const TXL_LDS_AS bf16x8 *)(blk + lane_off);
+}
+// col_frag over the 32 rows starting at byte `blk` (a 16-row-aligned block)
+// with a precomputed tr_lane_off; hi = false leaves k-slots 4..7 zero.
+__device__ __forceinline__ bf16x8 col_frag_at(const TXL_LDS_AS char *blk, int lane_off, bool hi = true)
+{
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(blk + lane_off));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    u32x2 h2 = {0u, 0u};
+    if (hi) h2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (TXL_LDS_AS i16x4 *)(blk + 16 * CPR * 16 + lane_off)));
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+// One half of col_frag_at (rows 4 g + e of the block at `blk`), as 2 dwords.
+__device__ __forceinline__ u32x2 tr_half(const TXL_LDS_AS char *blk, int lane_off)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(blk + lane_off)));
+}
+__device__ __forceinline__ const TXL_LDS_AS char *lds_bytes(const u32x4 *tile)
+{
+    return (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)tile;
+}
+
 // Two C-layout MFMA results (4 rows each per lane) as one 8-slot bf16 operand.
 __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b)
 {

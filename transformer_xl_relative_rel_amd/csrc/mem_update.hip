@@ -17,40 +17,38 @@ namespace txl {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kUnroll = 4;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;      // 16-byte words per thread
 
-__global__ __launch_bounds__(256) void mem_update_kernel(MemUpdateArgs a)
+// grid: x over the 16-byte words of one batch row's new memory, y over
+// (buffer, batch row).  Every load of a thread is issued before its stores.
+__global__ __launch_bounds__(kThreads) void mem_update_kernel(MemUpdateArgs a)
 {
-    const int buf = blockIdx.y;
-    const unsigned char *mem = a.mem[buf];
-    const unsigned char *hh = a.h[buf];
-    unsigned char *dst = a.dst[buf];
-    const int64_t per_batch = (int64_t)a.M_new * a.row_chunks;
-    const int64_t total = per_batch * a.B;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < total; base += stride * kUnroll) {
-        u32x4 val[kUnroll];
-        unsigned char *out[kUnroll];
+    const int buf = (int)blockIdx.y / a.B;
+    const int b = (int)blockIdx.y - buf * a.B;
+    const unsigned char *mem = a.mem[buf] ? a.mem[buf] + b * a.mem_bs : nullptr;
+    const unsigned char *hh = a.h[buf] + b * a.h_bs;
+    unsigned char *dst = a.dst[buf] + b * a.new_bs;
+    const uint32_t per_batch = (uint32_t)a.M_new * (uint32_t)a.row_chunks;
+    const uint32_t rc = (uint32_t)a.row_chunks;
+    const uint32_t e0 = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 val[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t e = base + u * stride;
-            out[u] = nullptr;
-            if (e < total) {
-                const int b = (int)(e / per_batch);
-                const int64_t rem = e - (int64_t)b * per_batch;
-                const int t = (int)(rem / a.row_chunks);          // row of the new memory
-                const int c = (int)(rem - (int64_t)t * a.row_chunks);
-                const int src_row = a.beg + t;                      // row of cat([mem; h])
-                const unsigned char *src = (src_row < a.M_cur)
-                    ? mem + b * a.mem_bs + ((int64_t)src_row * a.row_chunks + c) * 16
-                    : hh + b * a.h_bs + ((int64_t)(src_row - a.M_cur) * a.row_chunks + c) * 16;
-                val[u] = *reinterpret_cast<const u32x4 *>(src);
-                out[u] = dst + b * a.new_bs + ((int64_t)t * a.row_chunks + c) * 16;
-            }
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t e = e0 + u * kThreads;
+        if (e < per_batch) {
+            const uint32_t t = e / rc;                  // row of the new memory
+            const uint32_t c = e - t * rc;
+            const int src_row = a.beg + (int)t;         // row of cat([mem; h])
+            const unsigned char *src = (src_row < a.M_cur) ? mem + ((int64_t)src_row * rc + c) * 16
+                                                           : hh + ((int64_t)(src_row - a.M_cur) * rc + c) * 16;
+            val[u] = *reinterpret_cast<const u32x4 *>(src);
         }
+    }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (out[u]) *reinterpret_cast<u32x4 *>(out[u]) = val[u];
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t e = e0 + u * kThreads;
+        if (e < per_batch) *reinterpret_cast<u32x4 *>(dst + (int64_t)e * 16) = val[u];
     }
 }
 
@@ -58,11 +56,11 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemUpdateArgs a)
 
 hipError_t launch_mem_update(const MemUpdateArgs &a, hipStream_t s)
 {
-    const int64_t total = (int64_t)a.M_new * a.row_chunks * a.B;
-    if (total == 0 || a.n_buf == 0) return hipSuccess;
-    int64_t blocks = (total + 256 * kUnroll - 1) / (256 * kUnroll);
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(mem_update_kernel, dim3((unsigned)blocks, (unsigned)a.n_buf), dim3(256), 0, s, a);
+    const int64_t per_batch = (int64_t)a.M_new * a.row_chunks;
+    if (per_batch == 0 || a.n_buf == 0 || a.B == 0) return hipSuccess;
+    if (per_batch >= ((int64_t)1 << 31) || (int64_t)a.n_buf * a.B > 65535) return hipErrorInvalidValue;
+    const int64_t blocks = (per_batch + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+    hipLaunchKernelGGL(mem_update_kernel, dim3((unsigned)blocks, (unsigned)(a.n_buf * a.B)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

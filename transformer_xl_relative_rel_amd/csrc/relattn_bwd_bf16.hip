@@ -220,14 +220,35 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     auto store_g = [&](int kt) {
         if (!qok) return;
         const int pb = L - 1 - iq + kt * BK + 4 * g;
+        uint16_t *gp = grow + pb;
+        if (kt * BK + BK - 1 <= i0w + M) {
+            // every key of the tile is visible to every query of the wave: all columns < K
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+            for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int p = pb + 16 * tt + v;
-                if (p < K) grow[p] = bf16_bits(gprev[tt][v]);
-            }
+                for (int v = 0; v < 4; ++v) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (pb + 16 * tt + v < K) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
+        }
     };
+    // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
+    const int rlo0 = row_lane_off(0, g, n), rlo1 = row_lane_off(1, g, n);
+    int trl[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
+    // Skew columns of row n that the position part reads but no key of the
+    // tile fills: [n + 1, 16) and [80, n + 81), 16 per row; lane (g, n) zeroes
+    // four of them after the band values there have served their purpose.
+    int zoff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int k = 4 * g + e;
+        zoff[e] = rowb + (k < 15 - n ? n + 1 + k : 80 + k - (15 - n));
+    }
     for (int kt = 0; kt < ntile; ++kt) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -238,25 +259,30 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         if (kt >= 1 && kt - 1 < ntile_w) store_g(kt - 1);
         if (kt >= ntile_w) continue;
         const int j0 = kt * BK;
-        const u32x4 *tk = sk[kt & 1], *tv = sv[kt & 1];
+        const TXL_LDS_AS char *tk = lds_bytes(sk[kt & 1]);
+        const TXL_LDS_AS char *tv = lds_bytes(sv[kt & 1]);
+        auto ring_blk = [&](int x0) {   // 16-row block of ring rows x0 .. x0 + 15 (x0 % 16 == 0)
+            return lds_bytes(sr[(x0 >> 6) & (RQ - 1)]) + (x0 & 63) * (CPR * 16);
+        };
 
         // band: T^T = R_band . (c (q + vb))^T - lse2, masked band rows at -inf
         const int thi = M + i0w - j0 + 15;
         const int tlo = win > 0 ? M + 1 - win + i0w - j0 + 15 : -(1 << 30);
+        const bool bmask = thi < 16 * NBT - 1 || tlo > 0;
         f32x4 acc[NBT];
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
-            const int x0 = xw + 64 * kt + 16 * bt;   // wave-uniform, multiple of 16
-            const u32x4 *rq = sr[(x0 >> 6) & (RQ - 1)];
-            const int rr = (x0 & 63) + n;
-            f32x4 cin;
+            const TXL_LDS_AS char *rb = ring_blk(xw + 64 * kt + 16 * bt);
+            f32x4 cin = {nlse, nlse, nlse, nlse};
+            if (bmask) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = 16 * bt + 4 * g + v;
-                cin[v] = (row > thi || row < tlo) ? -INFINITY : nlse;
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * bt + 4 * g + v;
+                    if (row > thi || row < tlo) cin[v] = -INFINITY;
+                }
             }
-            acc[bt] = mfma(row_frag(rq, rr, 0, g), qv[0], cin);
-            acc[bt] = mfma(row_frag(rq, rr, 1, g), qv[1], acc[bt]);
+            acc[bt] = mfma(row_frag_at(rb, rlo0), qv[0], cin);
+            acc[bt] = mfma(row_frag_at(rb, rlo1), qv[1], acc[bt]);
         }
         lds_order();
 #pragma unroll
@@ -271,22 +297,23 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         // content on top of the skewed band: log2-domain score minus lse
         f32x4 sc[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 cin = *reinterpret_cast<const f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (j0 + 16 * tt + 4 * g + v < kmem_abs) cin[v] = -INFINITY;
-            sc[tt] = cin;
-        }
+        for (int tt = 0; tt < NT; ++tt) sc[tt] = *reinterpret_cast<const f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g);
         lds_order();
+        if (kmem_abs > j0) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (j0 + 16 * tt + 4 * g + v < kmem_abs) sc[tt][v] = -INFINITY;
+        }
         f32x4 gs[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-            f32x4 s = mfma(row_frag(tk, 16 * tt + n, 0, g), qu[0], sc[tt]);
-            s = mfma(row_frag(tk, 16 * tt + n, 1, g), qu[1], s);
+            f32x4 s = mfma(row_frag_at(tk + tt * 16 * CPR * 16, rlo0), qu[0], sc[tt]);
+            s = mfma(row_frag_at(tk + tt * 16 * CPR * 16, rlo1), qu[1], s);
             f32x4 dp = {nD, nD, nD, nD};
-            dp = mfma(row_frag(tv, 16 * tt + n, 0, g), dof[0], dp);
-            dp = mfma(row_frag(tv, 16 * tt + n, 1, g), dof[1], dp);
+            dp = mfma(row_frag_at(tv + tt * 16 * CPR * 16, rlo0), dof[0], dp);
+            dp = mfma(row_frag_at(tv + tt * 16 * CPR * 16, rlo1), dof[1], dp);
 #pragma unroll
             for (int v = 0; v < 4; ++v) gs[tt][v] = __builtin_amdgcn_exp2f(s[v]) * dp[v];
         }
@@ -295,46 +322,33 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         for (int ch = 0; ch < NT / 2; ++ch) {
             const bf16x8 gf = pack8(gs[2 * ch], gs[2 * ch + 1]);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) dqu[dt] = mfma(col_frag(tk, 32 * ch, dt, g, n), gf, dqu[dt]);
+            for (int dt = 0; dt < NDT; ++dt) dqu[dt] = mfma(col_frag_at(tk + ch * 32 * CPR * 16, trl[dt]), gf, dqu[dt]);
         }
-        // dS into the skew row at key positions, read back at band positions
+        // dS into the skew row at key positions (columns 16..79), zeros in the
+        // row's other read positions; read back at band positions
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g) = gs[tt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) skw[zoff[e]] = 0.f;
         lds_order();
         // position part: dq^T += R_band^T . G^T over band rows 0..79 in three
         // k-steps (band rows 32 ks + {4g + e, 16 + 4g + e}; rows >= 80 are zero)
-        auto ring_tr = [&](int cc, int dt) -> u32x2 {
-            const int x = xw + 64 * kt + cc;
-            const u32x4 *rq = sr[(x >> 6) & (RQ - 1)];
-            const int r = x & 63;
-            TXL_LDS_AS char *base = (TXL_LDS_AS char *)(TXL_LDS_AS void *)rq;
-            const int chunk = 2 * dt + ((n >> 1) & 1);
-            const int off = (r * CPR + (chunk ^ swz(r))) * 16 + 8 * (n & 1);
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(base + off)));
-        };
 #pragma unroll
         for (int ks = 0; ks < 3; ++ks) {
             f32x8 gv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int cc = 32 * ks + 4 * g + e;
-                const int jj = cc + n - 15;
-                const float x = skw[rowb + cc + n + 1];
-                gv[e] = (jj >= 0 && jj < BK) ? x : 0.f;
-                if (ks < 2) {
-                    const float y = skw[rowb + cc + 16 + n + 1];
-                    gv[4 + e] = (jj + 16 >= 0 && jj + 16 < BK) ? y : 0.f;
-                } else {
-                    gv[4 + e] = 0.f;
-                }
+                gv[e] = skw[rowb + 32 * ks + 4 * g + e + n + 1];
+                gv[4 + e] = ks < 2 ? skw[rowb + 32 * ks + 16 + 4 * g + e + n + 1] : 0.f;
             }
             const bf16x8 gt = __builtin_convertvector(gv, bf16x8);
+            const TXL_LDS_AS char *blo = ring_blk(xw + 64 * kt + 32 * ks);
+            const TXL_LDS_AS char *bhi = ring_blk(xw + 64 * kt + 32 * ks + 16);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const u32x2 lo = ring_tr(32 * ks + 4 * g + (n >> 2), dt);
-                const u32x2 hi = ks < 2 ? ring_tr(32 * ks + 16 + 4 * g + (n >> 2), dt) : u32x2{0u, 0u};
-                const bf16x8 rt = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                dqv[dt] = mfma(rt, gt, dqv[dt]);
+                const u32x2 lo = tr_half(blo, trl[dt]);
+                const u32x2 hi = ks < 2 ? tr_half(bhi, trl[dt]) : u32x2{0u, 0u};
+                dqv[dt] = mfma(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), gt, dqv[dt]);
             }
         }
         lds_order();
@@ -487,6 +501,12 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
     // band tiles of this wave: query rows 16 s2 .. +15, band columns 16 pt .. +15
     const int s2 = wave & 1;
     const int pt0 = 3 * (wave >> 1);
+    // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
+    const int rlo0 = row_lane_off(0, g, n), rlo1 = row_lane_off(1, g, n);
+    int trl[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
+    constexpr int BLK16 = 16 * CPR * 16;   // bytes of 16 tile rows
     for (int s = 0; s < nsteps; ++s) {
         const int i0 = ibeg + QS * s;
         const int buf = s & 1;
@@ -496,33 +516,40 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
             issue(s + 1);
             load_seg(nsteps - 2 - s);
         }
+        const TXL_LDS_AS char *tqu = lds_bytes(squ[buf]);
+        const TXL_LDS_AS char *tqv = lds_bytes(sqv[buf]);
+        const TXL_LDS_AS char *tdo = lds_bytes(sdo[buf]);
         // T[i][c] = c (q_i + vb) . r[pw + c] - lse2_i for the step's queries,
         // with pw the r row of (last query, first key); masked entries -inf
         const int pw = L - 1 - (i0 + QS - 1) + j0;
         {
-            const bf16x8 qa0 = row_frag(sqv[buf], 16 * s2 + n, 0, g);
-            const bf16x8 qa1 = row_frag(sqv[buf], 16 * s2 + n, 1, g);
+            const bf16x8 qa0 = row_frag_at(tqv + s2 * BLK16, rlo0);
+            const bf16x8 qa1 = row_frag_at(tqv + s2 * BLK16, rlo1);
             f32x4 nl;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * s2 + 4 * g + v;
-                nl[v] = (i0 + r < L) ? -sl2[buf][r] : -INFINITY;
+            for (int v = 0; v < 4; ++v) nl[v] = -sl2[buf][16 * s2 + 4 * g + v];
+            // masking needed: rows past L, r rows past K-1 (causal) or below K - window
+            const bool qmask = i0 + QS > L;
+            const bool cmask = pw + 16 * (pt0 + 3) - 1 > K - 1 || (win > 0 && pw + 16 * pt0 < K - win);
+            if (qmask) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (i0 + 16 * s2 + 4 * g + v >= L) nl[v] = -INFINITY;
             }
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int pt = pt0 + u;
-                const int pc = pw + 16 * pt + n;            // this lane's r row
-                const u32x4 *seg = sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)];
-                const bf16x8 rb0 = row_frag(seg, 16 * (pt & 1) + n, 0, g);
-                const bf16x8 rb1 = row_frag(seg, 16 * (pt & 1) + n, 1, g);
-                const bool cm = pc > K - 1 || (win > 0 && pc < K - win);
-                f32x4 cin;
+                const TXL_LDS_AS char *seg =
+                    lds_bytes(sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)]) + (pt & 1) * BLK16;
+                f32x4 cin = nl;
+                if (cmask) {
+                    const int pc = pw + 16 * pt + n;            // this lane's r row
+                    if (pc > K - 1 || (win > 0 && pc < K - win)) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                }
+                f32x4 acc = mfma(qa0, row_frag_at(seg, rlo0), cin);
+                acc = mfma(qa1, row_frag_at(seg, rlo1), acc);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) cin[v] = cm ? -INFINITY : nl[v];
-                f32x4 acc = mfma(qa0, rb0, cin);
-                acc = mfma(qa1, rb1, acc);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[v];
+                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * pt + n] = acc[v];
             }
         }
         __syncthreads();
@@ -535,15 +562,15 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * x + 4 * g + v;
                 cin[v] = tband[r * TS + 16 * wave + n - r + QS - 1];
-                if (jw < kmem_abs) cin[v] = -INFINITY;
             }
-            f32x4 sc = mfma(row_frag(squ[buf], 16 * x + n, 0, g), kf[0], cin);
-            sc = mfma(row_frag(squ[buf], 16 * x + n, 1, g), kf[1], sc);
+            if (jw < kmem_abs) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            f32x4 sc = mfma(row_frag_at(tqu + x * BLK16, rlo0), kf[0], cin);
+            sc = mfma(row_frag_at(tqu + x * BLK16, rlo1), kf[1], sc);
             f32x4 dp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) dp[v] = -sdd[buf][16 * x + 4 * g + v];
-            dp = mfma(row_frag(sdo[buf], 16 * x + n, 0, g), vf[0], dp);
-            dp = mfma(row_frag(sdo[buf], 16 * x + n, 1, g), vf[1], dp);
+            dp = mfma(row_frag_at(tdo + x * BLK16, rlo0), vf[0], dp);
+            dp = mfma(row_frag_at(tdo + x * BLK16, rlo1), vf[1], dp);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 p[x][v] = __builtin_amdgcn_exp2f(sc[v]);
@@ -554,8 +581,8 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         const bf16x8 gb = pack8(gs[0], gs[1]);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            dvt[dt] = mfma(col_frag(sdo[buf], 0, dt, g, n), pb, dvt[dt]);
-            dkt[dt] = mfma(col_frag(squ[buf], 0, dt, g, n), gb, dkt[dt]);
+            dvt[dt] = mfma(col_frag_at(tdo, trl[dt]), pb, dvt[dt]);
+            dkt[dt] = mfma(col_frag_at(tqu, trl[dt]), gb, dkt[dt]);
         }
     }
 
@@ -626,6 +653,10 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     f32x4 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int trg = tr_lane_off(psub, g, n);
+    int trl[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
     u32x4 gr, qr;
     if (nsteps > 0) fetch(0, gr, qr);
     for (int t = 0; t < nsteps; ++t) {
@@ -634,9 +665,9 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
         sq[bg][lrow * CPR + lpos] = qr;
         __syncthreads();
         if (t + 1 < nsteps) fetch(t + 1, gr, qr);
-        const bf16x8 ga = col_frag(sg[bg], 0, psub, g, n);
+        const bf16x8 ga = col_frag_at(lds_bytes(sg[bg]), trg);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag(sq[bg], 0, dt, g, n), acc[dt]);
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag_at(lds_bytes(sq[bg]), trl[dt]), acc[dt]);
     }
     if (bg > 0) {
 #pragma unroll

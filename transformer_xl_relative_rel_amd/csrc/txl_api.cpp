@@ -360,6 +360,9 @@ static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur
     const int end = M_cur + (L - ext_len > 0 ? L - ext_len : 0);
     const int beg = end - mem_len > 0 ? end - mem_len : 0;
     const int mnew = end - beg;
+    if ((int64_t)mnew * (int64_t)(row / 16) >= ((int64_t)1 << 31) || (int64_t)n_buf * B > 65535)
+        return fail(TXL_ERR_UNSUPPORTED, "one batch row of the new memory must hold < 2^31 16-byte words and "
+                    "n_buf * B must be <= 65535");
     if (mem_bs < 0 || h_bs < 0 || new_bs < 0) return fail(TXL_ERR_INVALID_ARG, "negative batch stride");
     if ((mem_bs * (int64_t)es) % 16 || (h_bs * (int64_t)es) % 16 || (new_bs * (int64_t)es) % 16)
         return fail(TXL_ERR_INVALID_ARG, "batch strides must keep 16-byte alignment");
