@@ -80,6 +80,59 @@ def recorded_traffic(kernel_src):
     return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
 
 
+def stack_flops(B, L, M, d, H, dh, di):
+    """Algorithmic flops of one post-LN layer on one segment (GEMMs + attention)."""
+    K = M + L
+    HD = H * dh
+    gemm = 2 * B * L * d * HD + 2 * B * K * d * 2 * HD + 2 * K * d * HD + 2 * B * L * HD * d + 2 * 2 * B * L * d * di
+    return gemm + flops_alg(B, H, L, M, dh)
+
+
+def stack_bench(torch, txl):
+    """16 post-LN layers (d 1024, H 16, dh 64, d_inner 4096), B 4, eight
+    segments of L 512 with mem_len 512: every segment runs the whole stack and
+    the memory update of all 17 buffers.  Weights N(0, 0.02) bf16 (seeded on
+    the device), LayerNorm gamma 1 beta 0, biases 0, embeddings N(0, 1); one
+    untimed pass over the segments first, then the eight segments between two
+    events on the stream."""
+    n_layer, d, H, dh, di, B, L, mem_len, segs = 16, 1024, 16, 64, 4096, 4, 512, 512, 8
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1111)
+    w = lambda *sh: (torch.randn(*sh, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    layers = [{"W_qkv": w(3 * H * dh, d), "W_r": w(H * dh, d), "W_o": w(d, H * dh),
+               "ln1_g": torch.ones(d, device=dev), "ln1_b": torch.zeros(d, device=dev), "W1": w(di, d),
+               "b1": torch.zeros(di, device=dev), "W2": w(d, di), "b2": torch.zeros(d, device=dev),
+               "ln2_g": torch.ones(d, device=dev), "ln2_b": torch.zeros(d, device=dev)} for _ in range(n_layer)]
+    u = torch.randn(H, dh, generator=gen, device=dev) * 0.02
+    vb = torch.randn(H, dh, generator=gen, device=dev) * 0.02
+    xs = [torch.randn(B, L, d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(segs)]
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(txl.layer_workspace_size(xs[0], layers[0], H, dh, mem_len), dtype=torch.uint8, device=dev)
+
+    def run():
+        mems = None
+        for x in xs:
+            _, mems = txl.stack_segment(x, mems, layers, u, vb, H, dh, mem_len, workspace=ws, stream=stream)
+        return mems
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    F = n_layer * (stack_flops(B, L, 0, d, H, dh, di) + (segs - 1) * stack_flops(B, L, mem_len, d, H, dh, di))
+    print(json.dumps({"metric": "16-layer stack forward, 8 segments end to end", "value": round(ms, 3), "unit": "ms",
+                      "higher_is_better": False, "tflops_alg": round(F / (ms * 1e-3) / 1e12, 1),
+                      "flops": F, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "stack L16 d1024 H16 dh64 d_inner4096 B4 L512 mem512 x8 segments",
+                                 "n_layer": n_layer, "B": B, "L": L, "mem_len": mem_len, "segments": segs}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +140,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--stack", action="store_true",
+                    help="instead of the attention step, time the 16-layer stack workload (B4, d1024, H16, "
+                         "d_inner 4096, 8 segments of L512 with mem_len 512) end to end")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one Tail_M copy of this many MiB (bigger than every cache) so that a "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE pass can calibrate its counters against known bytes")
@@ -100,6 +156,10 @@ def main():
 
     import transformer_xl_relative_rel_amd as txl
     from transformer_xl_relative_rel_amd import synth
+
+    if args.stack:
+        stack_bench(torch, txl)
+        return
 
     dev = "cuda:0"
     B, H, L, M, dh = 8, 16, 512, 512, 64

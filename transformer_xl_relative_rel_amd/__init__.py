@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "relattn_bwd",
-    "relattn_bwd_workspace_size", "mem_update", "mem_update_batched",
+    "relattn_bwd_workspace_size", "mem_update", "mem_update_batched", "stack_segment",
     "layer_fwd", "layer_workspace_size", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
 
@@ -338,3 +338,27 @@ def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, *, eps: float
     _check(lib().txl_layer_fwd(ctypes.byref(desc), ctypes.byref(lw), _ptr(h_in), _ptr(mem if M_cur else None), M_cur,
                                _ptr(u), _ptr(vb), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def stack_segment(x, mems, layers: list, u, vb, n_head: int, d_head: int, mem_len: int, *, eps: float = 1e-5,
+                  workspace=None, stream=None):
+    """One segment through a layer stack, as [SRC] MemTransformerLM._forward
+    followed by _update_mems: hids[0] = x, hids[n+1] = txl_layer_fwd(hids[n],
+    mems[n]), then every memory is replaced by the Tail of [mems[n]; hids[n]]
+    in one txl_mem_update_batched call.  Only sequences the library calls.
+
+    x [B, L, d] bf16; mems: None (first segment) or a list of len(layers) + 1
+    tensors [B, M_cur, d] bf16; layers: weight dicts as for layer_fwd.
+    Returns (hids, new_mems); hids[-1] is the stack output.
+    """
+    import torch
+    M_cur = 0 if mems is None else mems[0].shape[1]
+    if workspace is None:
+        need = layer_workspace_size(x, layers[0], n_head, d_head, M_cur, eps)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    hids = [x]
+    for n, w in enumerate(layers):
+        hids.append(layer_fwd(hids[n], None if mems is None else mems[n], w, u, vb, n_head, d_head, eps=eps,
+                              workspace=workspace, stream=stream))
+    new_mems = mem_update_batched(mems, hids, mem_len, stream=stream)
+    return hids, new_mems

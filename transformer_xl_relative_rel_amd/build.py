@@ -23,12 +23,13 @@ ARCH = "gfx950"
 # Packed-fp32 VALU instructions are disabled for all device code.
 DEVICE_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
-# Per-source extras.  The bf16 attention kernel runs one wave per SIMD with
-# close to 512 registers: MFMA results stay in VGPRs (no AGPR round trips for
-# the softmax and the skew stores), and its scores are finite or -inf by
+# Per-source extras.  The bf16 attention kernels keep MFMA results in VGPRs
+# (no AGPR round trips for the softmax, the skew stores and the accumulators
+# the loop body touches), and the forward's scores are finite or -inf by
 # construction, so max() needs no NaN canonicalisation.
 EXTRA = {
     "relattn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "relattn_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

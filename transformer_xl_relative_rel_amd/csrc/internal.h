@@ -77,9 +77,11 @@ struct RelAttnBwdArgs {
     uint16_t *qu, *qv;      // [B*H][L][64] bf16: c (q + u), c (q + vb)
     float *dd, *lse2;       // [B*H][L]: rowsum(dout * out), lse * log2(e)
     uint16_t *g;            // [B*H][L][kp] bf16: dS of (i, j) at column L-1-i+j
-    float *bias_part;       // [B*H][nqblk][2][64]: per 16-query block sums of dq's two parts
+    float *bias_part;       // [nsplit][B*H][nqblk][2][64]: per 16-query block sums of dq's two parts
+    float *dq_part;         // [nsplit][B*H][L][64] fp32 partial dq of each key split (nsplit > 1)
     int kp;                 // row stride of g (K rounded up to 64)
     int nqblk;              // 16-query blocks per head
+    int nsplit, tps;        // key splits of the dq kernel and key tiles per split
 };
 
 size_t relattn_bwd_workspace_bytes(int B, int H, int L, int M);

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace txl {
@@ -25,29 +27,58 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 
 // [SRC] PositionalEmbedding: row c of [K][d] is position p = K-1-c;
 // columns [0, d/2) are sin(p f_t), [d/2, d) are cos(p f_t), f_t = 10000^(-2t/d).
-__global__ void pos_emb_kernel(uint16_t *out, int K, int d, int clamp_len)
+// Thread (t, row block): f_t once in fp64, then for each row the angle p f_t
+// in fp64, reduced to [-pi, pi] in fp64 (two-part 2 pi), sin and cos of the
+// reduced angle in fp32 (error ~1e-7, far below the bf16 rounding of the
+// stored value).
+constexpr int POS_ROWS = 4;    // rows per workgroup
+__global__ __launch_bounds__(256) void pos_emb_kernel(uint16_t *out, int K, int d, int clamp_len)
 {
     const int half = d / 2;
-    const int64_t total = (int64_t)K * half;
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)(e / half), t = (int)(e - (int64_t)c * half);
-        int p = K - 1 - c;
-        if (clamp_len > 0 && p > clamp_len) p = clamp_len;
-        const double f = exp(-(2.0 * t / d) * 9.210340371976184);   // ln(10000)
-        const double ang = p * f;
-        out[(int64_t)c * d + t] = f32_to_bf16((float)sin(ang));
-        out[(int64_t)c * d + half + t] = f32_to_bf16((float)cos(ang));
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= half) return;
+    const double f = exp(-(2.0 * t / d) * 9.210340371976184);   // ln(10000)
+    const double two_pi_hi = 6.283185307179586, two_pi_lo = 2.4492935982947064e-16;
+    for (int c0 = blockIdx.y * POS_ROWS; c0 < K; c0 += gridDim.y * POS_ROWS) {
+        const int c1 = min(K, c0 + POS_ROWS);
+        for (int c = c0; c < c1; ++c) {
+            int p = K - 1 - c;
+            if (clamp_len > 0 && p > clamp_len) p = clamp_len;
+            const double ang = p * f;
+            const double k = rint(ang / two_pi_hi);
+            const float red = (float)((ang - k * two_pi_hi) - k * two_pi_lo);
+            float sv, cv;
+            sincosf(red, &sv, &cv);
+            out[(int64_t)c * d + t] = f32_to_bf16(sv);
+            out[(int64_t)c * d + half + t] = f32_to_bf16(cv);
+        }
     }
 }
 
-// y = max(x + b, 0) rounded to bf16; x [N][n] fp32, b [n] fp32 (may be NULL).
-__global__ void bias_relu_kernel(const float *x, const float *b, uint16_t *y, int64_t N, int n)
+// y = max(x + b, 0) rounded to bf16; x [N][n] fp32, b [n] fp32 (may be NULL);
+// n a multiple of 8.  Each thread moves 8 consecutive values.
+__global__ __launch_bounds__(256) void bias_relu_kernel(const float *x, const float *b, uint16_t *y, int64_t N, int n)
 {
-    const int64_t total = N * n;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const int n8 = n / 8;
+    const int64_t total = N * n8;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int col = (int)(e % n);
-        float v = x[e] + (b ? b[col] : 0.f);
-        y[e] = f32_to_bf16(v > 0.f ? v : 0.f);
+        const int64_t row = e / n8;
+        const int col = (int)(e - row * n8) * 8;
+        const f32x4v *xp = reinterpret_cast<const f32x4v *>(x + row * n + col);
+        f32x4v v0 = xp[0], v1 = xp[1];
+        if (b) {
+            v0 += *reinterpret_cast<const f32x4v *>(b + col);
+            v1 += *reinterpret_cast<const f32x4v *>(b + col + 4);
+        }
+        u32x4v o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float lo = k < 2 ? v0[2 * k] : v1[2 * k - 4], hi = k < 2 ? v0[2 * k + 1] : v1[2 * k - 3];
+            o[k] = (uint32_t)f32_to_bf16(lo > 0.f ? lo : 0.f) | ((uint32_t)f32_to_bf16(hi > 0.f ? hi : 0.f) << 16);
+        }
+        *reinterpret_cast<u32x4v *>(y + row * n + col) = o;
     }
 }
 
@@ -122,13 +153,17 @@ int layer_norm_max_width() { return LN_THREADS * LN_MAXV; }
 
 hipError_t launch_pos_emb(uint16_t *out, int K, int d, int clamp_len, hipStream_t s)
 {
-    hipLaunchKernelGGL(pos_emb_kernel, dim3(grid_for((int64_t)K * (d / 2))), dim3(256), 0, s, out, K, d, clamp_len);
+    if (K <= 0 || d < 2) return hipSuccess;
+    const int ry = std::min((K + POS_ROWS - 1) / POS_ROWS, 65535);
+    hipLaunchKernelGGL(pos_emb_kernel, dim3((unsigned)((d / 2 + 255) / 256), (unsigned)ry), dim3(256), 0, s, out, K, d,
+                       clamp_len);
     return hipGetLastError();
 }
 
 hipError_t launch_bias_relu(const float *x, const float *b, uint16_t *y, int64_t N, int n, hipStream_t s)
 {
-    hipLaunchKernelGGL(bias_relu_kernel, dim3(grid_for(N * n)), dim3(256), 0, s, x, b, y, N, n);
+    if (n % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bias_relu_kernel, dim3(grid_for(N * (n / 8))), dim3(256), 0, s, x, b, y, N, n);
     return hipGetLastError();
 }
 

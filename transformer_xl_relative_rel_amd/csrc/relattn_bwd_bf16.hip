@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bf16_tiles.h"
 #include "internal.h"
 
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     const int g = lane >> 4, n = lane & 15;
     const int BH = a.B * a.H, L = a.L, M = a.M, K = a.K;
     const int nqb = (L + QROWS - 1) / QROWS;
-    const int wg = blockIdx.x;
+    const int split = blockIdx.x % a.nsplit;
+    const int wg = blockIdx.x / a.nsplit;
     const int qblk = nqb - 1 - wg / BH;            // the longest query blocks first
     const int bh = wg - (wg / BH) * BH;
     const int b = bh / a.H, h = bh - b * a.H;
@@ -143,7 +146,9 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     const int i0w = i0 + 16 * wave;
     const int iq = i0w + n;
     const bool qok = iq < L;
-    const int ntile = (min(i0 + QROWS - 1, L - 1) + M) / BK + 1;
+    // key tiles [kt0, kt1) of this split; the wave's own queries see tiles below ntile_w
+    const int kt0 = split * a.tps;
+    const int kt1 = min((min(i0 + QROWS - 1, L - 1) + M) / BK + 1, kt0 + a.tps);
     const int ntile_w = i0w < L ? (min(i0w + 15, L - 1) + M) / BK + 1 : 0;
 
     // per-lane query operands and row constants
@@ -206,9 +211,11 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqu[dt] = dqv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_kv(0);
+    if (kt0 < kt1) {
+        load_kv(kt0);
 #pragma unroll
-    for (int q = 0; q < RQ - 1; ++q) load_r_quarter(q);
+        for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
+    }
     float *skw = sskew[wave];
     const int rowb = skew_row(n);
     uint16_t *grow = a.g + ((int64_t)bh * L + iqc) * a.kp;
@@ -249,14 +256,14 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         const int k = 4 * g + e;
         zoff[e] = rowb + (k < 15 - n ? n + 1 + k : 80 + k - (15 - n));
     }
-    for (int kt = 0; kt < ntile; ++kt) {
+    for (int kt = kt0; kt < kt1; ++kt) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (kt + 1 < ntile) {
+        if (kt + 1 < kt1) {
             load_kv(kt + 1);
             load_r_quarter(kt + RQ - 1);
         }
-        if (kt >= 1 && kt - 1 < ntile_w) store_g(kt - 1);
+        if (kt > kt0 && kt - 1 < ntile_w) store_g(kt - 1);
         if (kt >= ntile_w) continue;
         const int j0 = kt * BK;
         const TXL_LDS_AS char *tk = lds_bytes(sk[kt & 1]);
@@ -356,20 +363,25 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) gprev[tt] = gs[tt];
     }
-    if (ntile_w == ntile) store_g(ntile - 1);
+    if (kt1 > kt0 && kt1 - 1 < ntile_w) store_g(kt1 - 1);
 
     const float scale = a.scale;
-    if (qok) {
+    if (qok && a.nsplit == 1) {
         uint16_t *dqp = static_cast<uint16_t *>(a.dq) + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const bf16x4 y = __builtin_convertvector((dqu[dt] + dqv[dt]) * scale, bf16x4);
             *reinterpret_cast<u32x2 *>(dqp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, y);
         }
+    } else if (qok) {
+        // this split's part of dq (zeros when none of its tiles is visible to the query)
+        float *pp = a.dq_part + (((int64_t)split * BH + bh) * L + iq) * DH;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(pp + 16 * dt + 4 * g) = (dqu[dt] + dqv[dt]) * scale;
     }
     if (i0w < L) {
         // sums over the 16 queries of this wave (queries past L contribute 0)
-        float *part = a.bias_part + ((int64_t)bh * a.nqblk + i0w / 16) * (2 * DH);
+        float *part = a.bias_part + (((int64_t)split * BH + bh) * a.nqblk + i0w / 16) * (2 * DH);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -691,18 +703,18 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
 }
 
 // du, dvb: the per-block partial sums of one head, 16 waves each summing every
-// 16th (batch row, block) item, then the 16 wave sums in wave order.
+// 16th block of every (split, batch row), then the 16 wave sums in wave order.
 __global__ __launch_bounds__(1024) void bwd_bias_kernel(RelAttnBwdArgs a)
 {
     __shared__ float red[16][DH];
     const int h = blockIdx.x >> 1, which = blockIdx.x & 1;
     const int t = threadIdx.x, wave = t >> 6, d = t & 63;
-    const int nitems = a.B * a.nqblk;
     float s = 0.f;
-#pragma unroll 4
-    for (int it = wave; it < nitems; it += 16) {
-        const int b = it / a.nqblk, k = it - b * a.nqblk;
-        s += a.bias_part[((int64_t)(b * a.H + h) * a.nqblk + k) * (2 * DH) + which * DH + d];
+    for (int sb = 0; sb < a.nsplit * a.B; ++sb) {       // (split, b) in order; blocks k = wave (mod 16)
+        const int sp = sb / a.B, b = sb - sp * a.B;
+        const float *pp = a.bias_part + ((int64_t)sp * a.B * a.H + b * a.H + h) * a.nqblk * (2 * DH) + which * DH + d;
+#pragma unroll 2
+        for (int k = wave; k < a.nqblk; k += 16) s += pp[(int64_t)k * 2 * DH];
     }
     red[wave][d] = s;
     __syncthreads();
@@ -713,10 +725,40 @@ __global__ __launch_bounds__(1024) void bwd_bias_kernel(RelAttnBwdArgs a)
     }
 }
 
+// dq of split key ranges: the fp32 parts added in split order, rounded to bf16.
+// 16 threads per row (4 columns each), 16 rows per workgroup.
+__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(RelAttnBwdArgs a)
+{
+    const int64_t rows = (int64_t)a.B * a.H * a.L;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int c4 = (threadIdx.x & 15) * 4;
+    if (row >= rows) return;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < a.nsplit; ++sp) s += *reinterpret_cast<const f32x4 *>(a.dq_part + (sp * rows + row) * DH + c4);
+    const int bh = (int)(row / a.L), i = (int)(row - (int64_t)bh * a.L);
+    const int b = bh / a.H, h = bh - b * a.H;
+    uint16_t *dqp = static_cast<uint16_t *>(a.dq) + b * a.qs[0] + h * a.qs[1] + (int64_t)i * a.qs[2] + c4;
+    *reinterpret_cast<u32x2 *>(dqp) = __builtin_bit_cast(u32x2, __builtin_convertvector(s, bf16x4));
+}
+
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Key splits of the dq kernel: enough workgroups for one per CU (the kernel's
+// LDS allows one), each split at least one key tile.
+void dq_split_plan(int B, int H, int L, int M, int &nsplit, int &tps)
+{
+    const int nqb = (L + QROWS - 1) / QROWS;
+    const int ntile = (L - 1 + M) / BK + 1;
+    const int64_t base = (int64_t)B * H * nqb;
+    int s = base >= 256 ? 1 : (int)std::min<int64_t>(ntile, (256 + base - 1) / base);
+    if (s < 1) s = 1;
+    tps = (ntile + s - 1) / s;
+    nsplit = (ntile + tps - 1) / tps;
+}
+
 struct BwdLayout {
-    size_t qu, qv, dd, lse2, part, g, total;
+    size_t qu, qv, dd, lse2, part, dqp, g, total;
+    int nsplit, tps;
 };
 
 BwdLayout bwd_layout(int B, int H, int L, int M)
@@ -726,12 +768,14 @@ BwdLayout bwd_layout(int B, int H, int L, int M)
     const size_t kp = (size_t)((K + BK - 1) / BK) * BK;
     const size_t nqblk = (size_t)(L + 15) / 16;
     BwdLayout l{};
+    dq_split_plan(B, H, L, M, l.nsplit, l.tps);
     size_t off = 0;
     l.qu = off; off += round256(rows * DH * 2);
     l.qv = off; off += round256(rows * DH * 2);
     l.dd = off; off += round256(rows * 4);
     l.lse2 = off; off += round256(rows * 4);
-    l.part = off; off += round256((size_t)B * H * nqblk * 2 * DH * 4);
+    l.part = off; off += round256((size_t)l.nsplit * B * H * nqblk * 2 * DH * 4);
+    l.dqp = off; off += l.nsplit > 1 ? round256((size_t)l.nsplit * rows * DH * 4) : 0;
     l.g = off; off += round256(rows * kp * 2);
     l.total = off;
     return l;
@@ -750,6 +794,9 @@ void relattn_bwd_carve(RelAttnBwdArgs &a, void *ws)
     a.dd = reinterpret_cast<float *>(base + l.dd);
     a.lse2 = reinterpret_cast<float *>(base + l.lse2);
     a.bias_part = reinterpret_cast<float *>(base + l.part);
+    a.dq_part = l.nsplit > 1 ? reinterpret_cast<float *>(base + l.dqp) : nullptr;
+    a.nsplit = l.nsplit;
+    a.tps = l.tps;
     a.g = reinterpret_cast<uint16_t *>(base + l.g);
     a.kp = ((a.K + BK - 1) / BK) * BK;
     a.nqblk = (a.L + 15) / 16;
@@ -760,7 +807,9 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     const int64_t rows = (int64_t)a.B * a.H * a.L;
     const int BH = a.B * a.H;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS))), dim3(QTHR), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS) * a.nsplit)), dim3(QTHR), 0, s, a);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(bwd_dq_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + BK - 1) / BK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
     hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);

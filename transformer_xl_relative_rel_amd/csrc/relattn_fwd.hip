@@ -441,15 +441,14 @@ __global__ __launch_bounds__(256) void relattn_fwd_kernel(RelAttnArgs a)
 // One pass over the splits in chunks of CH whose loads are issued together
 // (one memory latency per chunk); the running sums are rescaled when a chunk
 // raises the running max.  The order is fixed, so the result is bitwise
-// deterministic.  One wave per block.
-template <bool BF, int DH>
-__global__ __launch_bounds__(64) void relattn_combine_kernel(RelAttnArgs a)
+// deterministic.  CH = 4 serves up to four splits in one chunk.
+template <bool BF, int DH, int CH>
+__global__ __launch_bounds__(256) void relattn_combine_kernel(RelAttnArgs a)
 {
     using T = typename Elem<BF>::T;
     constexpr int TPR = DH / 4;                     // threads per query row
-    constexpr int CH = 16;                          // splits loaded together
     const int BH = a.B * a.H;
-    const int64_t row = (int64_t)blockIdx.x * (64 / TPR) + threadIdx.x / TPR;
+    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
     const int c4 = (threadIdx.x % TPR) * 4;
     if (row >= (int64_t)BH * a.L) return;
     const int bh = (int)(row / a.L), iq = (int)(row - (int64_t)bh * a.L);
@@ -508,20 +507,27 @@ hipError_t launch_one(const RelAttnArgs &a, hipStream_t s)
 
 }  // namespace
 
+template <bool BF, int DH>
+void launch_combine_dh(const RelAttnArgs &a, dim3 grid, hipStream_t s)
+{
+    if (a.nsplit <= 4) hipLaunchKernelGGL((relattn_combine_kernel<BF, DH, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((relattn_combine_kernel<BF, DH, 16>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s)
 {
     const int64_t rows = (int64_t)a.B * a.H * a.L;
-    const int rows_per_block = 64 / (dh / 4);
+    const int rows_per_block = 256 / (dh / 4);
     const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
     if (dtype == 1) {
-        if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<true, 32>), grid, dim3(64), 0, s, a);
-        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<true, 64>), grid, dim3(64), 0, s, a);
-        else if (dh == 128) hipLaunchKernelGGL((relattn_combine_kernel<true, 128>), grid, dim3(64), 0, s, a);
+        if (dh == 32) launch_combine_dh<true, 32>(a, grid, s);
+        else if (dh == 64) launch_combine_dh<true, 64>(a, grid, s);
+        else if (dh == 128) launch_combine_dh<true, 128>(a, grid, s);
         else return hipErrorInvalidValue;
     } else {
-        if (dh == 16) hipLaunchKernelGGL((relattn_combine_kernel<false, 16>), grid, dim3(64), 0, s, a);
-        else if (dh == 32) hipLaunchKernelGGL((relattn_combine_kernel<false, 32>), grid, dim3(64), 0, s, a);
-        else if (dh == 64) hipLaunchKernelGGL((relattn_combine_kernel<false, 64>), grid, dim3(64), 0, s, a);
+        if (dh == 16) launch_combine_dh<false, 16>(a, grid, s);
+        else if (dh == 32) launch_combine_dh<false, 32>(a, grid, s);
+        else if (dh == 64) launch_combine_dh<false, 64>(a, grid, s);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -174,9 +174,12 @@ txl_status txl_layer_fwd(const txl_layer_desc *d, const txl_layer_weights *w, co
     for (const void *p : mats)
         if (p && (reinterpret_cast<uintptr_t>(p) & 15u))
             return fail(TXL_ERR_INVALID_ARG, "matrices and activations must be 16-byte aligned");
-    const float *vecs[] = {w->ln1_g, w->ln1_b, w->b1, w->b2, w->ln2_g, w->ln2_b, u, vb};
+    const float *vecs[] = {w->ln1_g, w->ln1_b, w->b1, w->b2, w->ln2_g, w->ln2_b};
     for (const float *p : vecs)
-        if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return fail(TXL_ERR_INVALID_ARG, "fp32 vectors must be 4-byte aligned");
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u))
+            return fail(TXL_ERR_INVALID_ARG, "LayerNorm and bias vectors must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(vb)) & 3u)
+        return fail(TXL_ERR_INVALID_ARG, "u and vb must be 4-byte aligned");
 
     txl_relattn_desc ad;
     attn_desc(*d, M_cur, ad);
