@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "bf16_tiles.h"
 #include "internal.h"
@@ -224,23 +225,16 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     // after that iteration's loads, so that the wait for the next tile's loads
     // does not also wait for stores issued just before it.
     f32x4 gprev[NT];
+    // Every column a tile can produce, L-1-i+j for j up to the wave's last key
+    // tile end, is below K + 78 <= kp, so rows are stored whole: columns >= K
+    // (keys past i + M, dS = 0) land in the row's padding, which dr ignores.
     auto store_g = [&](int kt) {
         if (!qok) return;
-        const int pb = L - 1 - iq + kt * BK + 4 * g;
-        uint16_t *gp = grow + pb;
-        if (kt * BK + BK - 1 <= i0w + M) {
-            // every key of the tile is visible to every query of the wave: all columns < K
+        uint16_t *gp = grow + (L - 1 - iq + kt * BK + 4 * g);
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (pb + 16 * tt + v < K) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
-        }
+            for (int v = 0; v < 4; ++v) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
     };
     // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
     const int rlo0 = row_lane_off(0, g, n), rlo1 = row_lane_off(1, g, n);
@@ -272,25 +266,35 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
             return lds_bytes(sr[(x0 >> 6) & (RQ - 1)]) + (x0 & 63) * (CPR * 16);
         };
 
-        // band: T^T = R_band . (c (q + vb))^T - lse2, masked band rows at -inf
+        // band: T^T = R_band . (c (q + vb))^T - lse2, masked band rows at -inf;
+        // all fragment reads first, then the MFMAs
         const int thi = M + i0w - j0 + 15;
         const int tlo = win > 0 ? M + 1 - win + i0w - j0 + 15 : -(1 << 30);
-        const bool bmask = thi < 16 * NBT - 1 || tlo > 0;
         f32x4 acc[NBT];
+        auto band = [&](auto MASKED) {
+            bf16x8 rf[NBT][2];
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) {
-            const TXL_LDS_AS char *rb = ring_blk(xw + 64 * kt + 16 * bt);
-            f32x4 cin = {nlse, nlse, nlse, nlse};
-            if (bmask) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * bt + 4 * g + v;
-                    if (row > thi || row < tlo) cin[v] = -INFINITY;
-                }
+            for (int bt = 0; bt < NBT; ++bt) {
+                const TXL_LDS_AS char *rb = ring_blk(xw + 64 * kt + 16 * bt);
+                rf[bt][0] = row_frag_at(rb, rlo0);
+                rf[bt][1] = row_frag_at(rb, rlo1);
             }
-            acc[bt] = mfma(row_frag_at(rb, rlo0), qv[0], cin);
-            acc[bt] = mfma(row_frag_at(rb, rlo1), qv[1], acc[bt]);
-        }
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) {
+                f32x4 cin = {nlse, nlse, nlse, nlse};
+                if constexpr (decltype(MASKED)::value) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int row = 16 * bt + 4 * g + v;
+                        if (row > thi || row < tlo) cin[v] = -INFINITY;
+                    }
+                }
+                acc[bt] = mfma(rf[bt][0], qv[0], cin);
+                acc[bt] = mfma(rf[bt][1], qv[1], acc[bt]);
+            }
+        };
+        if (thi < 16 * NBT - 1 || tlo > 0) band(std::true_type{});
+        else band(std::false_type{});
         lds_order();
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
@@ -548,21 +552,30 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
                 for (int v = 0; v < 4; ++v)
                     if (i0 + 16 * s2 + 4 * g + v >= L) nl[v] = -INFINITY;
             }
+            bf16x8 rb[3][2];
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int pt = pt0 + u;
                 const TXL_LDS_AS char *seg =
                     lds_bytes(sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)]) + (pt & 1) * BLK16;
+                rb[u][0] = row_frag_at(seg, rlo0);
+                rb[u][1] = row_frag_at(seg, rlo1);
+            }
+            f32x4 acc[3];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
                 f32x4 cin = nl;
                 if (cmask) {
-                    const int pc = pw + 16 * pt + n;            // this lane's r row
+                    const int pc = pw + 16 * (pt0 + u) + n;      // this lane's r row
                     if (pc > K - 1 || (win > 0 && pc < K - win)) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                 }
-                f32x4 acc = mfma(qa0, row_frag_at(seg, rlo0), cin);
-                acc = mfma(qa1, row_frag_at(seg, rlo1), acc);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * pt + n] = acc[v];
+                acc[u] = mfma(qa0, rb[u][0], cin);
+                acc[u] = mfma(qa1, rb[u][1], acc[u]);
             }
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[u][v];
         }
         __syncthreads();
         // scores, probabilities and dS of this wave's 16 keys
@@ -743,6 +756,10 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(RelAttnBwdArgs a)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Row stride of the stored score gradients: columns reach K + 77 (see the dq
+// kernel's G stores), rounded up to 64.
+int g_row_stride(int K) { return ((K + 78 + BK - 1) / BK) * BK; }
+
 // Key splits of the dq kernel: enough workgroups for one per CU (the kernel's
 // LDS allows one), each split at least one key tile.
 void dq_split_plan(int B, int H, int L, int M, int &nsplit, int &tps)
@@ -765,7 +782,7 @@ BwdLayout bwd_layout(int B, int H, int L, int M)
 {
     const size_t rows = (size_t)B * H * L;
     const int K = M + L;
-    const size_t kp = (size_t)((K + BK - 1) / BK) * BK;
+    const size_t kp = (size_t)g_row_stride(K);
     const size_t nqblk = (size_t)(L + 15) / 16;
     BwdLayout l{};
     dq_split_plan(B, H, L, M, l.nsplit, l.tps);
@@ -798,7 +815,7 @@ void relattn_bwd_carve(RelAttnBwdArgs &a, void *ws)
     a.nsplit = l.nsplit;
     a.tps = l.tps;
     a.g = reinterpret_cast<uint16_t *>(base + l.g);
-    a.kp = ((a.K + BK - 1) / BK) * BK;
+    a.kp = g_row_stride(a.K);
     a.nqblk = (a.L + 15) / 16;
 }
 
