@@ -149,3 +149,33 @@ def test_bwd_full_size_one_head(B, H, L, M, h):
     got_h = {"dq": got["dq"][:, h:h + 1], "dk": got["dk"][:, h:h + 1], "dv": got["dv"][:, h:h + 1],
              "dr": got["dr"][h:h + 1], "du": got["du"][h:h + 1], "dvb": got["dvb"][h:h + 1]}
     check(got_h, want, f"B{B} H{H} L{L} M{M} h{h}")
+
+
+def test_bwd_strided_views_of_fused_qkv():
+    """q, k, v as head views of one fused [B, K, 3, H, dh] projection buffer and
+    out / dout in the merged-heads layout [B, L, H, dh] (the layout a decoder
+    layer hands over); gradients come back with the same strides."""
+    B, H, L, M = 2, 3, 70, 50
+    K = M + L
+    log(f"case: bwd strided B{B} H{H} L{L} M{M}")
+    d = inputs(B, H, L, M, 0.5)
+    qkv = torch.zeros((B, K, 3, H, 64), dtype=torch.bfloat16, device=DEV)
+    qkv[:, M:, 0] = dev(d["q"], torch.bfloat16).permute(0, 2, 1, 3)
+    qkv[:, :, 1] = dev(d["k"], torch.bfloat16).permute(0, 2, 1, 3)
+    qkv[:, :, 2] = dev(d["v"], torch.bfloat16).permute(0, 2, 1, 3)
+    q = qkv[:, M:, 0].permute(0, 2, 1, 3)
+    k = qkv[:, :, 1].permute(0, 2, 1, 3)
+    v = qkv[:, :, 2].permute(0, 2, 1, 3)
+    r = dev(d["r"], torch.bfloat16)
+    u, vb = dev(d["u"], torch.float32), dev(d["vb"], torch.float32)
+    out_m = torch.empty((B, L, H, 64), dtype=torch.bfloat16, device=DEV)
+    out = out_m.permute(0, 2, 1, 3)
+    _, lse = txl.relattn_fwd(q, k, v, r, u, vb, out=out, want_lse=True)
+    dout_m = dev(d["dout"], torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    dout = dout_m.permute(0, 2, 1, 3)
+    grads = txl.relattn_bwd(q, k, v, r, u, vb, out, lse, dout)
+    torch.cuda.synchronize()
+    assert grads[0].stride() == q.stride() and grads[1].stride() == k.stride()
+    got = {n: t.float().cpu().numpy().astype(np.float64) for n, t in zip(NAMES, grads)}
+    want = oracle.relattn_bwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], d["dout"], threads=8)
+    check(got, want, "strided")

@@ -64,6 +64,7 @@ constexpr int NBT = NT + 1;      // band tiles per 16-query block (79 rows)
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
 constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
 constexpr int TILE_CH = BK * CPR;
+constexpr int BLK16B = 16 * CPR * 16;   // bytes of 16 tile rows
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -628,16 +629,17 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 // ---------------------------------------------------------------------------
 // dr: one workgroup per 64 rows of r, 16 waves: wave w takes rows
 // 16 (w % 4) .. + 15 of the tile for the batch rows b = w / 4 (mod 4); the
-// four batch groups stage their own tiles, prefetched one step ahead in
-// registers, and their sums are added in group order at the end.
+// four batch groups stage their own 64-query steps, prefetched one step ahead
+// in registers, and their sums are added in group order at the end.
 
 constexpr int RW = 16;
 constexpr int RG = 4;               // batch groups
+constexpr int RQS = 64;             // queries per step
 
 __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
 {
-    __shared__ __attribute__((aligned(16))) u32x4 sg[RG][QT_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 sq[RG][QT_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sg[RG][RQS * CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 sq[RG][RQS * CPR];
     __shared__ __attribute__((aligned(16))) f32x4 red[RG - 1][4 * NDT * 64];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -649,16 +651,14 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     const int h = blockIdx.x / nkb;
     const int p0 = BK * (blockIdx.x - h * nkb);
     const int tg = psub * 64 + lane;              // thread within the batch group
-    const int lrow = tg / CPR, lpos = tg & (CPR - 1);
-    const int lc = lpos ^ swz(lrow);              // chunk this thread moves
+    const int lrow = tg / CPR, lpos = tg & (CPR - 1);   // rows lrow and lrow + 32 of a step
+    const int lc0 = lpos ^ swz(lrow), lc1 = lpos ^ swz(lrow + 32);
     // rows i with a column >= L-1-i in [p0, p0 + 63]
     const int ilo = L - 1 - (p0 + BK - 1) > 0 ? ((L - 1 - (p0 + BK - 1)) / QS) * QS : 0;
-    const int nch = (L - ilo + QS - 1) / QS;
+    const int nch = (L - ilo + RQS - 1) / RQS;
     const int nsteps = ((a.B + RG - 1) / RG) * nch;   // same count for every group
 
-    auto fetch = [&](int t, u32x4 &gr, u32x4 &qr) {
-        const int b = bg + RG * (t / nch);
-        const int i = ilo + QS * (t % nch) + lrow;
+    auto fetch_row = [&](int b, int i, int lc, u32x4 &gr, u32x4 &qr) {
         gr = u32x4{0u, 0u, 0u, 0u};
         qr = u32x4{0u, 0u, 0u, 0u};
         if (b < a.B && i < L) {
@@ -674,6 +674,12 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
             }
         }
     };
+    auto fetch = [&](int t, u32x4 (&gr)[2], u32x4 (&qr)[2]) {
+        const int b = bg + RG * (t / nch);
+        const int i = ilo + RQS * (t % nch) + lrow;
+        fetch_row(b, i, lc0, gr[0], qr[0]);
+        fetch_row(b, i + 32, lc1, gr[1], qr[1]);
+    };
 
     f32x4 acc[NDT];
 #pragma unroll
@@ -682,17 +688,24 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     int trl[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
-    u32x4 gr, qr;
+    u32x4 gr[2], qr[2];
     if (nsteps > 0) fetch(0, gr, qr);
     for (int t = 0; t < nsteps; ++t) {
         __syncthreads();
-        sg[bg][lrow * CPR + lpos] = gr;
-        sq[bg][lrow * CPR + lpos] = qr;
+        sg[bg][lrow * CPR + lpos] = gr[0];
+        sq[bg][lrow * CPR + lpos] = qr[0];
+        sg[bg][(lrow + 32) * CPR + lpos] = gr[1];
+        sq[bg][(lrow + 32) * CPR + lpos] = qr[1];
         __syncthreads();
         if (t + 1 < nsteps) fetch(t + 1, gr, qr);
-        const bf16x8 ga = col_frag_at(lds_bytes(sg[bg]), trg);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag_at(lds_bytes(sq[bg]), trl[dt]), acc[dt]);
+        for (int half = 0; half < 2; ++half) {
+            const TXL_LDS_AS char *tgb = lds_bytes(sg[bg]) + half * 2 * BLK16B;
+            const TXL_LDS_AS char *tqb = lds_bytes(sq[bg]) + half * 2 * BLK16B;
+            const bf16x8 ga = col_frag_at(tgb, trg);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag_at(tqb, trl[dt]), acc[dt]);
+        }
     }
     if (bg > 0) {
 #pragma unroll
@@ -702,14 +715,14 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     if (bg == 0) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            f32x4 s = acc[dt];
+            f32x4 sum = acc[dt];
 #pragma unroll
-            for (int k = 0; k < RG - 1; ++k) s += red[k][(psub * NDT + dt) * 64 + lane];
+            for (int k = 0; k < RG - 1; ++k) sum += red[k][(psub * NDT + dt) * 64 + lane];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int p = p0 + 16 * psub + 4 * g + v;
                 // dr = scale sum dS (q + vb) = ln 2 sum dS c (q + vb)
-                if (p < K) a.dr[((int64_t)h * K + p) * DH + 16 * dt + n] = s[v] * LN2;
+                if (p < K) a.dr[((int64_t)h * K + p) * DH + 16 * dt + n] = sum[v] * LN2;
             }
         }
     }
