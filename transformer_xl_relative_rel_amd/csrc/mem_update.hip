@@ -21,7 +21,9 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;      // 16-byte words per thread
 
 // grid: x over the 16-byte words of one batch row's new memory, y over
-// (buffer, batch row).  Every load of a thread is issued before its stores.
+// (buffer, batch row).  Every load of a thread is issued before its stores;
+// both are non-temporal (streamed once, the new memory is next read a whole
+// segment later).
 __global__ __launch_bounds__(kThreads) void mem_update_kernel(MemUpdateArgs a)
 {
     const int buf = (int)blockIdx.y / a.B;
@@ -42,13 +44,13 @@ __global__ __launch_bounds__(kThreads) void mem_update_kernel(MemUpdateArgs a)
             const int src_row = a.beg + (int)t;         // row of cat([mem; h])
             const unsigned char *src = (src_row < a.M_cur) ? mem + ((int64_t)src_row * rc + c) * 16
                                                            : hh + ((int64_t)(src_row - a.M_cur) * rc + c) * 16;
-            val[u] = *reinterpret_cast<const u32x4 *>(src);
+            val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
         }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const uint32_t e = e0 + u * kThreads;
-        if (e < per_batch) *reinterpret_cast<u32x4 *>(dst + (int64_t)e * 16) = val[u];
+        if (e < per_batch) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4 *>(dst + (int64_t)e * 16));
     }
 }
 
