@@ -29,9 +29,9 @@
 //          G[i][c] = dS[i][c - (L-1-i)].  G is also stored to the workspace
 //          (row i, column c) for dr, and per-block sums of both dq parts go
 //          to the workspace for du and dvb.
-//   dkv  : one workgroup per 64 keys (4 waves of 16 keys), queries in steps of
-//          32, untransposed (queries on MFMA rows, keys on lanes).  The band
-//          T = c (q + vb) . R^T of the step's 32 queries and the 96 r rows
+//   dkv  : one workgroup per 128 keys (4 waves of 32 keys), queries in steps
+//          of 32, untransposed (queries on MFMA rows, keys on lanes).  The band
+//          T = c (q + vb) . R^T of the step's 32 queries and the 160 r rows
 //          they need (a ring of r rows in LDS, loaded a step ahead with the
 //          query tiles) is shared by the workgroup through LDS; each wave reads
 //          its skewed part, recomputes p and dS and accumulates
@@ -406,15 +406,20 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv
+// dk, dv: one workgroup per 128 keys, 4 waves of 32 keys (two 16-key
+// sub-tiles), queries in steps of 32.
 
-constexpr int KW = 4;               // waves per workgroup (16 keys each)
+constexpr int KW = 4;               // waves per workgroup
+constexpr int KPW = 32;             // keys per wave
+constexpr int KBLK = KW * KPW;      // keys per workgroup
 constexpr int QS = 32;              // queries per step
 constexpr int QT_CH = QS * CPR;     // chunks per query tile
-constexpr int TS = 97;              // band row stride in floats (96 used)
-constexpr int RSEG = 4;             // r ring segments of QS rows: three in use, one loading
+constexpr int NBC = (QS + KBLK) / 16;   // 16-column band tiles per step (r rows pw .. pw + 159)
+constexpr int TS = 16 * NBC + 4;    // band row stride in floats
+constexpr int RSEG = 8;             // r ring segments of QS rows: five in use, one loading
 constexpr int KTHR = 64 * KW;
 static_assert(QT_CH == KTHR, "one 16-byte load per thread per query tile");
+static_assert((2 * NBC) % KW == 0, "band tiles split evenly over the waves");
 
 __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 {
@@ -434,21 +439,24 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
     const int kb = wg / BH;                      // the key blocks seen by most queries first
     const int bh = wg - kb * BH;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int j0 = BK * kb;
-    const int jw = j0 + 16 * wave + n;           // this lane's key
-    const bool jok = jw < K;
-    const int jc = jok ? jw : 0;
+    const int j0 = KBLK * kb;
+    const int jw0 = j0 + KPW * wave;             // first key of this wave
 
     const uint16_t *kp = static_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
     const uint16_t *vp = static_cast<const uint16_t *>(a.v) + b * a.vs[0] + h * a.vs[1];
     const bf16x8 zero8 = {};
-    bf16x8 kf[NKK], vf[NKK];
+    bf16x8 kf[2][NKK], vf[2][NKK];               // [key sub-tile][k-step]: lane key jw0 + 16 kx + n
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kp + (int64_t)jc * a.ks[2] + 32 * kk + 8 * g);
-        const bf16x8 y = *reinterpret_cast<const bf16x8 *>(vp + (int64_t)jc * a.vs[2] + 32 * kk + 8 * g);
-        kf[kk] = jok ? x : zero8;
-        vf[kk] = jok ? y : zero8;
+    for (int kx = 0; kx < 2; ++kx) {
+        const int j = jw0 + 16 * kx + n;
+        const int jc = j < K ? j : 0;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kp + (int64_t)jc * a.ks[2] + 32 * kk + 8 * g);
+            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(vp + (int64_t)jc * a.vs[2] + 32 * kk + 8 * g);
+            kf[kx][kk] = j < K ? x : zero8;
+            vf[kx][kk] = j < K ? y : zero8;
+        }
     }
     int kmem_abs = 0;
     if (a.mem_valid) {
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
     // queries below j0 - M see no key of the block; a block entirely below the
     // valid memory is seen by nobody
     int ibeg = j0 - M > 0 ? ((j0 - M) / QS) * QS : 0;
-    if (kmem_abs >= j0 + BK) ibeg = L;
+    if (kmem_abs >= j0 + KBLK) ibeg = L;
     const int nsteps = ibeg < L ? (L - ibeg + QS - 1) / QS : 0;
 
     // loads of a query step: thread tid moves chunk tid of each 32-row tile
@@ -490,10 +498,10 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         if (wave == 1 && lane < QS / 4) load_lds16(ddrs, (uint32_t)((i0 + 4 * lane) * 4), sdd_base + (uint32_t)(s & 1) * (QS * 4));
     };
 
-    // r rows of the band: step s needs rows pw_s .. pw_s + 95 with
+    // r rows of the band: step s needs rows pw_s .. pw_s + 16 NBC - 1 with
     // pw_s = L - QS - i0_s + j0, which moves down by QS per step.  Ring segment
-    // sg (slot sg % RSEG) holds rows pwl + QS sg .. + QS - 1, pwl being pw of
-    // the last step; step s uses segments nsteps-1-s .. nsteps+1-s and loads
+    // sgm (slot sgm % RSEG) holds rows pwl + QS sgm .. + QS - 1, pwl being pw of
+    // the last step; step s uses segments nsteps-1-s .. nsteps+3-s and loads
     // segment nsteps-2-s for the next step.  Rows outside [0, K) read zeros.
     const uint16_t *rp = static_cast<const uint16_t *>(a.r) + h * a.rs[0];
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
@@ -505,25 +513,26 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
                    sring_base + (uint32_t)(sgm & (RSEG - 1)) * (QT_CH * 16));
     };
 
-    f32x4 dkt[NDT], dvt[NDT];
+    f32x4 dkt[2][NDT], dvt[2][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) dkt[dt] = dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) dkt[kx][dt] = dvt[kx][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (nsteps > 0) {
         issue(0);
-        load_seg(nsteps - 1);
-        load_seg(nsteps);
-        load_seg(nsteps + 1);
+#pragma unroll
+        for (int sg5 = 0; sg5 < NBC / 2; ++sg5) load_seg(nsteps - 1 + sg5);
     }
     // band tiles of this wave: query rows 16 s2 .. +15, band columns 16 pt .. +15
-    const int s2 = wave & 1;
-    const int pt0 = 3 * (wave >> 1);
+    constexpr int TPW = 2 * NBC / KW;     // band tiles per wave
+    const int s2 = (TPW * wave) / NBC;
+    const int pt0 = (TPW * wave) % NBC;
     // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
     const int rlo0 = row_lane_off(0, g, n), rlo1 = row_lane_off(1, g, n);
     int trl[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
-    constexpr int BLK16 = 16 * CPR * 16;   // bytes of 16 tile rows
     for (int s = 0; s < nsteps; ++s) {
         const int i0 = ibeg + QS * s;
         const int buf = s & 1;
@@ -540,31 +549,31 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         // with pw the r row of (last query, first key); masked entries -inf
         const int pw = L - 1 - (i0 + QS - 1) + j0;
         {
-            const bf16x8 qa0 = row_frag_at(tqv + s2 * BLK16, rlo0);
-            const bf16x8 qa1 = row_frag_at(tqv + s2 * BLK16, rlo1);
+            const bf16x8 qa0 = row_frag_at(tqv + s2 * BLK16B, rlo0);
+            const bf16x8 qa1 = row_frag_at(tqv + s2 * BLK16B, rlo1);
             f32x4 nl;
 #pragma unroll
             for (int v = 0; v < 4; ++v) nl[v] = -sl2[buf][16 * s2 + 4 * g + v];
             // masking needed: rows past L, r rows past K-1 (causal) or below K - window
             const bool qmask = i0 + QS > L;
-            const bool cmask = pw + 16 * (pt0 + 3) - 1 > K - 1 || (win > 0 && pw + 16 * pt0 < K - win);
+            const bool cmask = pw + 16 * (pt0 + TPW) - 1 > K - 1 || (win > 0 && pw + 16 * pt0 < K - win);
             if (qmask) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     if (i0 + 16 * s2 + 4 * g + v >= L) nl[v] = -INFINITY;
             }
-            bf16x8 rb[3][2];
+            bf16x8 rb[TPW][2];
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < TPW; ++u) {
                 const int pt = pt0 + u;
                 const TXL_LDS_AS char *seg =
-                    lds_bytes(sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)]) + (pt & 1) * BLK16;
+                    lds_bytes(sring[(nsteps - 1 - s + (pt >> 1)) & (RSEG - 1)]) + (pt & 1) * BLK16B;
                 rb[u][0] = row_frag_at(seg, rlo0);
                 rb[u][1] = row_frag_at(seg, rlo1);
             }
-            f32x4 acc[3];
+            f32x4 acc[TPW];
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < TPW; ++u) {
                 f32x4 cin = nl;
                 if (cmask) {
                     const int pc = pw + 16 * (pt0 + u) + n;      // this lane's r row
@@ -574,52 +583,75 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
                 acc[u] = mfma(qa1, rb[u][1], acc[u]);
             }
 #pragma unroll
-            for (int u = 0; u < 3; ++u)
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[u][v];
         }
         __syncthreads();
-        // scores, probabilities and dS of this wave's 16 keys
-        f32x4 p[2], gs[2];
+        // scores, probabilities and dS of this wave's 32 keys
+        bf16x8 qa[2][NKK], da[2][NKK];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            f32x4 cin;
+            qa[x][0] = row_frag_at(tqu + x * BLK16B, rlo0);
+            qa[x][1] = row_frag_at(tqu + x * BLK16B, rlo1);
+            da[x][0] = row_frag_at(tdo + x * BLK16B, rlo0);
+            da[x][1] = row_frag_at(tdo + x * BLK16B, rlo1);
+        }
+        f32x4 p[2][2], gs[2][2];                 // [query sub-tile][key sub-tile]
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * x + 4 * g + v;
-                cin[v] = tband[r * TS + 16 * wave + n - r + QS - 1];
-            }
-            if (jw < kmem_abs) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            f32x4 sc = mfma(row_frag_at(tqu + x * BLK16, rlo0), kf[0], cin);
-            sc = mfma(row_frag_at(tqu + x * BLK16, rlo1), kf[1], sc);
-            f32x4 dp;
+        for (int x = 0; x < 2; ++x) {
+            f32x4 nd;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) dp[v] = -sdd[buf][16 * x + 4 * g + v];
-            dp = mfma(row_frag_at(tdo + x * BLK16, rlo0), vf[0], dp);
-            dp = mfma(row_frag_at(tdo + x * BLK16, rlo1), vf[1], dp);
+            for (int v = 0; v < 4; ++v) nd[v] = -sdd[buf][16 * x + 4 * g + v];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                p[x][v] = __builtin_amdgcn_exp2f(sc[v]);
-                gs[x][v] = p[x][v] * dp[v];
+            for (int kx = 0; kx < 2; ++kx) {
+                f32x4 cin;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * x + 4 * g + v;
+                    cin[v] = tband[r * TS + KPW * wave + 16 * kx + n - r + QS - 1];
+                }
+                if (jw0 + 16 * kx + n < kmem_abs) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                f32x4 sc = mfma(qa[x][0], kf[kx][0], cin);
+                sc = mfma(qa[x][1], kf[kx][1], sc);
+                f32x4 dp = mfma(da[x][0], vf[kx][0], nd);
+                dp = mfma(da[x][1], vf[kx][1], dp);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    p[x][kx][v] = __builtin_amdgcn_exp2f(sc[v]);
+                    gs[x][kx][v] = p[x][kx][v] * dp[v];
+                }
             }
         }
-        const bf16x8 pb = pack8(p[0], p[1]);
-        const bf16x8 gb = pack8(gs[0], gs[1]);
+        bf16x8 pb[2], gb[2];
+#pragma unroll
+        for (int kx = 0; kx < 2; ++kx) {
+            pb[kx] = pack8(p[0][kx], p[1][kx]);
+            gb[kx] = pack8(gs[0][kx], gs[1][kx]);
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            dvt[dt] = mfma(col_frag_at(tdo, trl[dt]), pb, dvt[dt]);
-            dkt[dt] = mfma(col_frag_at(tqu, trl[dt]), gb, dkt[dt]);
+            const bf16x8 dot = col_frag_at(tdo, trl[dt]);
+            const bf16x8 qut = col_frag_at(tqu, trl[dt]);
+#pragma unroll
+            for (int kx = 0; kx < 2; ++kx) {
+                dvt[kx][dt] = mfma(dot, pb[kx], dvt[kx][dt]);
+                dkt[kx][dt] = mfma(qut, gb[kx], dkt[kx][dt]);
+            }
         }
     }
 
-    if (jok) {
-        uint16_t *dkp = static_cast<uint16_t *>(a.dk) + b * a.ks[0] + h * a.ks[1] + (int64_t)jw * a.ks[2];
-        uint16_t *dvp = static_cast<uint16_t *>(a.dv) + b * a.vs[0] + h * a.vs[1] + (int64_t)jw * a.vs[2];
+#pragma unroll
+    for (int kx = 0; kx < 2; ++kx) {
+        const int j = jw0 + 16 * kx + n;
+        if (j >= K) continue;
+        uint16_t *dkp = static_cast<uint16_t *>(a.dk) + b * a.ks[0] + h * a.ks[1] + (int64_t)j * a.ks[2];
+        uint16_t *dvp = static_cast<uint16_t *>(a.dv) + b * a.vs[0] + h * a.vs[1] + (int64_t)j * a.vs[2];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             // dk = scale sum dS (q + u) = (scale / c) sum dS c (q + u) = ln 2 sum dS qu
-            const bf16x4 yk = __builtin_convertvector(dkt[dt] * LN2, bf16x4);
-            const bf16x4 yv = __builtin_convertvector(dvt[dt], bf16x4);
+            const bf16x4 yk = __builtin_convertvector(dkt[kx][dt] * LN2, bf16x4);
+            const bf16x4 yv = __builtin_convertvector(dvt[kx][dt], bf16x4);
             *reinterpret_cast<u32x2 *>(dkp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yk);
             *reinterpret_cast<u32x2 *>(dvp + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yv);
         }
@@ -840,7 +872,7 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS) * a.nsplit)), dim3(QTHR), 0, s, a);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(bwd_dq_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + BK - 1) / BK))), dim3(KTHR), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
     hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);
     return hipGetLastError();
