@@ -141,3 +141,33 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(txl, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         txl.lib()
+
+
+def _bwd(d, ws=FAKE * 20, ws_bytes=1 << 40, **kw):
+    vp = ctypes.c_void_p
+    ptr = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, r=FAKE * 4, u=FAKE * 5, vb=FAKE * 6, out=FAKE * 7, lse=FAKE * 8,
+               dout=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11, dv=FAKE * 12, dr=FAKE * 13, du=FAKE * 14, dvb=FAKE * 15)
+    ptr.update(kw)
+    order = ("q", "k", "v", "r", "u", "vb", "out", "lse", "dout", "dq", "dk", "dv", "dr", "du", "dvb")
+    return txl.lib().txl_relattn_bwd(ctypes.byref(d) if d is not None else None, *[vp(ptr[x]) for x in order],
+                                     vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
+
+
+def test_relattn_bwd_rejects_bad_arguments():
+    """Every check of txl_relattn_bwd runs on the host and fails before any launch."""
+    lib = txl.lib()
+    assert _bwd(None) == EINVAL
+    assert _bwd(_desc(dh=32)) == EUNSUP                       # the backward is bf16 with dh = 64 only
+    assert _bwd(_desc(dh=64, dtype=txl.F32)) == EUNSUP
+    assert b"dh = 64" in lib.txl_last_error()
+    for name in ("q", "lse", "dout", "dq", "dr", "du", "dvb"):
+        assert _bwd(_desc(), **{name: 0}) == EINVAL, name
+    assert _bwd(_desc(), dq=FAKE * 10 + 8) == EINVAL           # misaligned output
+    assert _bwd(_desc(), ws=0) == EWS
+    assert _bwd(_desc(), ws_bytes=16) == EWS
+    assert _bwd(_desc(), ws=FAKE * 20 + 64) == EWS            # workspace must be 256-byte aligned
+    assert _bwd(_desc(), dq=FAKE) == EALIAS                    # dq on top of q
+    assert _bwd(_desc(), dk=FAKE * 10) == EALIAS               # two outputs overlap
+    n = ctypes.c_size_t(0)
+    assert lib.txl_relattn_bwd_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == OK and n.value > 0
+    assert lib.txl_relattn_bwd_workspace_size(ctypes.byref(_desc(dh=128)), ctypes.byref(n)) == EUNSUP
