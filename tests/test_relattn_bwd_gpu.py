@@ -85,6 +85,7 @@ CASES = [
     (2, 2, 40, 24, 0.5, 30, None),
     (2, 2, 40, 24, 0.5, 0, [5, 24]),
     (2, 1, 130, 70, 0.5, 50, [0, 33]),
+    (9, 2, 40, 30, 0.5, 0, None),          # batch rows not a multiple of the dr kernel's 4 batch groups
 ]
 
 

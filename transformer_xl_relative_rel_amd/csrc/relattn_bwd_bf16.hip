@@ -16,7 +16,7 @@
 //   dr_c = scale sum over b and (i, j) with L-1-i+j = c of dS_ij (q_i + vb)
 //   du = sum over b, i of the k part of dq_i, dvb = the same of its r part.
 //
-// Kernels (one stream, in order):
+// Kernels (one stream, in the order prep, dq, dr, dkv, bias):
 //   prep : c (q + u) and c (q + vb) rounded to bf16 exactly as the forward
 //          forms its query operands (c = scale log2 e), D_i, lse in log2 units.
 //   dq   : one wave per 16 queries, 8 waves per workgroup, keys in tiles of
@@ -39,7 +39,8 @@
 //          the step's query tiles through the transposing LDS read; P and dS
 //          pass from the score MFMA's result layout to the operand layout
 //          without data movement).
-//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r).
+//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r),
+//          launched right after dq.
 //   bias : du, dvb from the per-block sums, in a fixed order.
 // No atomics: every output element has one writer and a fixed summation
 // order, so results are bitwise reproducible.
@@ -661,7 +662,7 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 // ---------------------------------------------------------------------------
 // dr: one workgroup per 64 rows of r, 16 waves: wave w takes rows
 // 16 (w % 4) .. + 15 of the tile for the batch rows b = w / 4 (mod 4); the
-// four batch groups stage their own 64-query steps, prefetched one step ahead
+// four batch groups stage their own 64-query steps, prefetched two steps ahead
 // in registers, and their sums are added in group order at the end.
 
 constexpr int RW = 16;
@@ -690,27 +691,34 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     const int nch = (L - ilo + RQS - 1) / RQS;
     const int nsteps = ((a.B + RG - 1) / RG) * nch;   // same count for every group
 
-    auto fetch_row = [&](int b, int i, int lc, u32x4 &gr, u32x4 &qr) {
+    // A fetch only issues loads; the mask of never-written columns (below
+    // L-1-i: keys before the first; at or past K) is computed from the indices
+    // and applied when the data is written to LDS, so the loads stay in flight.
+    struct Fetch {
+        u32x4 g[2], q[2];
+        u32x4 keep[2];    // per 32-bit word: bits of the bf16 columns to keep
+    };
+    auto fetch_row = [&](int b, int i, int lc, u32x4 &gr, u32x4 &qr, u32x4 &keep) {
         gr = u32x4{0u, 0u, 0u, 0u};
         qr = u32x4{0u, 0u, 0u, 0u};
+        keep = u32x4{0u, 0u, 0u, 0u};
         if (b < a.B && i < L) {
             const int64_t bh = (int64_t)b * a.H + h;
             gr = *reinterpret_cast<const u32x4 *>(a.g + (bh * L + i) * a.kp + p0 + 8 * lc);
             qr = *reinterpret_cast<const u32x4 *>(a.qv + (bh * L + i) * DH + 8 * lc);
-            // columns below L-1-i (keys before the first) and at or past K were never written
             const int cmin = L - 1 - i;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int col = p0 + 8 * lc + e;
-                if (col < cmin || col >= K) gr[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                if (col >= cmin && col < K) keep[e >> 1] |= (e & 1) ? 0xffff0000u : 0x0000ffffu;
             }
         }
     };
-    auto fetch = [&](int t, u32x4 (&gr)[2], u32x4 (&qr)[2]) {
+    auto fetch = [&](int t, Fetch &f) {
         const int b = bg + RG * (t / nch);
         const int i = ilo + RQS * (t % nch) + lrow;
-        fetch_row(b, i, lc0, gr[0], qr[0]);
-        fetch_row(b, i + 32, lc1, gr[1], qr[1]);
+        fetch_row(b, i, lc0, f.g[0], f.q[0], f.keep[0]);
+        fetch_row(b, i + 32, lc1, f.g[1], f.q[1], f.keep[1]);
     };
 
     f32x4 acc[NDT];
@@ -720,16 +728,18 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     int trl[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
-    u32x4 gr[2], qr[2];
-    if (nsteps > 0) fetch(0, gr, qr);
-    for (int t = 0; t < nsteps; ++t) {
+    // two steps in flight: registers hold steps t + 1 and t + 2 while step t is computed
+    Fetch fa, fb;
+    if (nsteps > 0) fetch(0, fa);
+    if (nsteps > 1) fetch(1, fb);
+    auto step = [&](int t, Fetch &f) {
         __syncthreads();
-        sg[bg][lrow * CPR + lpos] = gr[0];
-        sq[bg][lrow * CPR + lpos] = qr[0];
-        sg[bg][(lrow + 32) * CPR + lpos] = gr[1];
-        sq[bg][(lrow + 32) * CPR + lpos] = qr[1];
+        sg[bg][lrow * CPR + lpos] = f.g[0] & f.keep[0];
+        sq[bg][lrow * CPR + lpos] = f.q[0];
+        sg[bg][(lrow + 32) * CPR + lpos] = f.g[1] & f.keep[1];
+        sq[bg][(lrow + 32) * CPR + lpos] = f.q[1];
         __syncthreads();
-        if (t + 1 < nsteps) fetch(t + 1, gr, qr);
+        if (t + 2 < nsteps) fetch(t + 2, f);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const TXL_LDS_AS char *tgb = lds_bytes(sg[bg]) + half * 2 * BLK16B;
@@ -738,6 +748,10 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag_at(tqb, trl[dt]), acc[dt]);
         }
+    };
+    for (int t = 0; t < nsteps; t += 2) {
+        step(t, fa);
+        if (t + 1 < nsteps) step(t + 1, fb);
     }
     if (bg > 0) {
 #pragma unroll
@@ -872,8 +886,9 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS) * a.nsplit)), dim3(QTHR), 0, s, a);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(bwd_dq_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
+    // dr right after dq, while the score gradients dq stored are freshest in the caches
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
