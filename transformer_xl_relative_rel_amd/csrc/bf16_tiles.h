@@ -1,5 +1,6 @@
-// Small device helpers for the bf16 MFMA kernels of the attention backward:
-// 16x16x32 bf16 MFMA, direct-to-LDS buffer loads, LDS tile addressing with a
+// Small device helpers shared by the bf16 attention kernels (forward and
+// backward): vector types, the 16x16x32 bf16 MFMA, direct-to-LDS buffer loads,
+// buffer resources, and (for the backward's tiles) LDS addressing with a
 // row-dependent chunk swizzle and the transposing LDS read.  Internal header.
 #pragma once
 

@@ -48,22 +48,13 @@
 
 #include <type_traits>
 
+#include "bf16_tiles.h"
 #include "internal.h"
 
 namespace txl {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr int DH = 64;
+using namespace tiles;   // vector types, DH = 64, CPR, LN2, mfma, direct-to-LDS loads, buffer resources
 constexpr int NW = 8;            // waves per workgroup (two per SIMD)
 constexpr int RUNQ = 32;         // queries per run (two 16-query blocks)
 constexpr int NX = 2;            // 16-query blocks per wave (one run)
@@ -81,14 +72,12 @@ constexpr int RQ = 4;            // ring quarters: three in use plus one loading
 // distinct banks.
 __device__ __forceinline__ int skew_row(int n) { return 80 * n + 12 * (n >> 2); }
 constexpr int SKEW = 80 * 15 + 12 * 3 + 96;   // floats per wave
-constexpr int CPR = DH / 8;      // 16-byte chunks per row
 constexpr int RP = 16 / CPR;     // rows per 256 bytes
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
 constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
 constexpr int TILE_CH = BK * CPR;              // chunks per K or V tile (and per ring quarter)
 constexpr int NTHR = NW * 64;
 constexpr int LPT = TILE_CH / NTHR;            // 16-byte loads per thread per tile
-constexpr float LN2 = 0.69314718055994530942f;
 constexpr float TAU = 8.0f;      // deferred-rescale threshold (log2 units)
 static_assert(RUNQ * (PAIRS - 1) + 16 * NRB <= 64 * (RQ - 1), "a ring must hold one tile's bands in RQ - 1 quarters");
 static_assert(LPT * NTHR == TILE_CH, "whole tiles per load round");
@@ -97,13 +86,6 @@ static_assert(LPT * NTHR == TILE_CH, "whole tiles per load round");
 // rows (transposing b64 reads of 4 rows x 32 bytes).
 __device__ __forceinline__ int swz_k(int r) { return ((unsigned)r / RP) & (CPR - 1); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 6) & (CPR - 1); }
-
-// Orders this wave's LDS accesses for the compiler without waiting: LDS
-// instructions of one wave execute in issue order, so a read issued after a
-// write sees it, also when another lane wrote it.
-__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t x16) { return __uint_as_float(x16 << 16); }
 
 __device__ __forceinline__ float row_max4(float x)
 {
@@ -114,44 +96,7 @@ __device__ __forceinline__ float row_max4(float x)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// Direct HBM -> LDS load of 16 bytes per lane through a buffer resource: lane
-// l of the wave writes LDS byte address lds + 16 l.  Byte offsets at or past
-// the resource's size (negative ones included, as unsigned) read zeros.
-// Written as inline assembly so that the compiler does not track the load:
-// its own tracking of direct-to-LDS loads makes it wait for them before any
-// LDS read it cannot prove disjoint, which defeats the prefetch.  The caller
-// waits (s_waitcnt vmcnt(0) and a barrier) before anything reads the target.
-// M0 is saved and restored around the load.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds)
-{
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(lds)
-        : "memory");
-}
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(LDS_AS const void *)p;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
 
 template <int X> using IC = std::integral_constant<int, X>;
 
@@ -268,7 +213,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
     // V^T fragments (A operands of P.V), read through the transposing LDS read
     bf16x8 vf[NT / 2][NDT];
     auto load_v = [&]() {
-        LDS_AS char *vb = (LDS_AS char *)(LDS_AS void *)t.sv;
+        TXL_LDS_AS char *vb = (TXL_LDS_AS char *)(TXL_LDS_AS void *)t.sv;
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch)
 #pragma unroll
@@ -279,8 +224,8 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
                 const int off0 = (row0 * CPR + (chunk ^ swz_v(row0))) * 16 + 8 * (n & 1);
                 const int row1 = row0 + 16;
                 const int off1 = (row1 * CPR + (chunk ^ swz_v(row1))) * 16 + 8 * (n & 1);
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off0));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off1));
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off1));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
             }
@@ -669,7 +614,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 // bits 1-2 of the row, which 32 ch and +16 leave alone.
 __device__ __forceinline__ void read_vt(bf16x8 (&vf)[NT / 2][NDT], const u32x4 *sv, int g, int n)
 {
-    LDS_AS char *vb = (LDS_AS char *)(LDS_AS void *)sv;
+    TXL_LDS_AS char *vb = (TXL_LDS_AS char *)(TXL_LDS_AS void *)sv;
     const int row0 = 4 * g + (n >> 2);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -677,9 +622,9 @@ __device__ __forceinline__ void read_vt(bf16x8 (&vf)[NT / 2][NDT], const u32x4 *
         const int off = (row0 * CPR + (chunk ^ swz_v(row0))) * 16 + 8 * (n & 1);
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off + ch * 32 * CPR * 16));
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off + ch * 32 * CPR * 16));
             const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off + (ch * 32 + 16) * CPR * 16));
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off + (ch * 32 + 16) * CPR * 16));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
             vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
         }
