@@ -154,6 +154,18 @@ __device__ __forceinline__ const TXL_LDS_AS char *lds_bytes(const u32x4 *tile)
     return (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)tile;
 }
 
+// Four floats to consecutive LDS words as four one-word stores.  Left alone the
+// compiler merges them into two-word stores (ds_write2_b32), which measured
+// about 10% slower in the forward kernel for the skew rows' lane pattern.
+__device__ __forceinline__ void lds_store4(float *dst, f32x4 v)
+{
+    volatile TXL_LDS_AS float *p = (volatile TXL_LDS_AS float *)dst;
+    p[0] = v[0];
+    p[1] = v[1];
+    p[2] = v[2];
+    p[3] = v[3];
+}
+
 // Two C-layout MFMA results (4 rows each per lane) as one 8-slot bf16 operand.
 __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b)
 {

@@ -299,13 +299,7 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         else band(std::false_type{});
         lds_order();
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) {
-            float *dst = skw + rowb + 16 * bt + 4 * g + n + 1;
-            dst[0] = acc[bt][0];
-            dst[1] = acc[bt][1];
-            dst[2] = acc[bt][2];
-            dst[3] = acc[bt][3];
-        }
+        for (int bt = 0; bt < NBT; ++bt) lds_store4(skw + rowb + 16 * bt + 4 * g + n + 1, acc[bt]);
         lds_order();
         // content on top of the skewed band: log2-domain score minus lse
         f32x4 sc[NT];

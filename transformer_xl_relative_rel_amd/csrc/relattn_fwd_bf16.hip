@@ -265,14 +265,8 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
             for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + 1 - h][kk], qv[kk], acc[bt]);
         lds_order();
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) {
-            // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
-            float *dst = skw + skew_row(n) + 16 * bt + 4 * g + n + 1;
-            dst[0] = acc[bt][0];
-            dst[1] = acc[bt][1];
-            dst[2] = acc[bt][2];
-            dst[3] = acc[bt][3];
-        }
+        for (int bt = 0; bt < NBT; ++bt)   // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
+            lds_store4(skw + skew_row(n) + 16 * bt + 4 * g + n + 1, acc[bt]);
         lds_order();
     };
     // B: content MFMA of block x on top of the skewed band values
@@ -750,13 +744,7 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
                 for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(f.rf[bt + 1 - x][kk], st.qv[x][kk], acc[bt]);
             lds_order();
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) {
-                float *dst = skw + skew_row(nn) + 16 * bt + 4 * gg + nn + 1;
-                dst[0] = acc[bt][0];
-                dst[1] = acc[bt][1];
-                dst[2] = acc[bt][2];
-                dst[3] = acc[bt][3];
-            }
+            for (int bt = 0; bt < NBT; ++bt) lds_store4(skw + skew_row(nn) + 16 * bt + 4 * gg + nn + 1, acc[bt]);
             lds_order();
         };
         auto stage_b = [&](auto X) {
