@@ -64,14 +64,16 @@ constexpr int NT = BK / 16;      // 16-key sub-tiles per tile
 constexpr int NBT = NT + 1;      // band tiles per 16-query block
 constexpr int NRB = NT + 2;      // band tiles per run (two blocks)
 constexpr int RQ = 4;            // ring quarters: three in use plus one loading
-// Skew buffer: row n (query n) starts at float 80 n + 12 (n / 4); it is
-// written at columns 1..95 and read at columns 16..79, and the rows are far
-// enough apart that no row's writes reach another row's read range.  With
-// these starts the 64 lanes of a skew store (row n, column c + n) and the
-// 16-lane groups of a skew load (row n, 16-byte aligned column) each hit 64
-// distinct banks.
-__device__ __forceinline__ int skew_row(int n) { return 80 * n + 12 * (n >> 2); }
-constexpr int SKEW = 80 * 15 + 12 * 3 + 96;   // floats per wave
+// Skew buffer: row n (query n) starts at float 80 n + 4 (n / 4); it is
+// written at columns 1..95 and read at columns 16..79, and consecutive rows
+// start at least 80 floats apart, so no row's writes reach another row's read
+// range.  One-word LDS stores are serviced 32 lanes at a time over 32 banks;
+// with these starts the 32 lanes of each half of a skew store (row n, column
+// c + 4 g + n, g = lane / 16) hit 32 distinct banks (starts 80 n + 12 (n / 4)
+// measured two extra cycles per store).  Row starts are multiples of 4, so the
+// 16-byte skew loads are aligned.
+__device__ __forceinline__ int skew_row(int n) { return 80 * n + 4 * (n >> 2); }
+constexpr int SKEW = 80 * 15 + 4 * 3 + 96;   // floats per wave
 constexpr int RP = 16 / CPR;     // rows per 256 bytes
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
 constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
