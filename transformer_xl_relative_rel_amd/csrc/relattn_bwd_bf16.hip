@@ -123,10 +123,13 @@ constexpr int RQ = 4;               // r ring quarters: three in use, one loadin
 static_assert(TILE_CH == QTHR, "one 16-byte load per thread per tile");
 static_assert(QROWS - 16 + 16 * NBT <= 64 * (RQ - 1), "a tile's bands fit in three ring quarters");
 
-// Skew row of query n (as the forward): written at columns 1..95, rows far
-// enough apart that one row's used columns never meet another's.
-__device__ __forceinline__ int skew_row(int n) { return 80 * n + 12 * (n >> 2); }
-constexpr int SKEW = 80 * 15 + 12 * 3 + 96;
+// Skew row of query n: row n uses columns min(n + 1, 16) .. n + 80, and rows
+// start 80 to 92 floats apart, so one row's used columns never meet another's.
+// The starts keep the one-word band stores (32 lanes over 32 banks per
+// cycle) and the 16-byte dS stores (8 lanes over 32 banks per cycle) free of
+// bank conflicts; starts are multiples of 4, so 16-byte accesses are aligned.
+__device__ __forceinline__ int skew_row(int n) { return 168 * (n >> 1) - 4 * ((n >> 2) & 1) + 80 * (n & 1); }
+constexpr int SKEW = 1252 + 96;   // skew_row(15) + 96 floats per wave
 
 __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 {
