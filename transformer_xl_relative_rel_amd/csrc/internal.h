@@ -24,7 +24,8 @@ struct RelAttnArgs {
     int nqb;          // query blocks of 16 * kWaves * rb rows
     int nsplit;       // key-range splits (1 = normalise in the kernel)
     int tiles_per_split;
-    int remap;        // 1: XCD-aware workgroup order (needs B*H % 8 == 0)
+    int remap;        // XCD-aware workgroup order: 0 none, 1 blocks of (b, h) pairs (B*H % 8 == 0),
+                      // 2 heads h = x (mod 8) of every batch row on XCD x (H % 8 == 0)
     const int *mem_valid;   // [B] valid memory rows per batch row, or NULL (all M)
     int window;             // > 0: query i sees keys j >= i + M + 1 - window
 };
@@ -43,6 +44,20 @@ __device__ __forceinline__ int key_lo(const RelAttnArgs &a, int b, int i)
         lo = w > lo ? w : lo;
     }
     return lo;
+}
+
+// Flat (b, h) index of the j-th pair that the XCD-aware order places on XCD x
+// (workgroup w runs on XCD w % 8).  With remap 2 every batch row of a head
+// runs on one XCD, so the head's r rows, which all batch rows read, are
+// fetched into one L2 only; with remap 1 each XCD owns B*H/8 consecutive pairs.
+__device__ __forceinline__ int xcd_pair(const RelAttnArgs &a, int x, int j)
+{
+    if (a.remap == 2) {
+        const int hx = a.H >> 3;
+        const int b = j / hx;
+        return b * a.H + (j - b * hx) * 8 + x;
+    }
+    return x * ((a.B * a.H) >> 3) + j;
 }
 
 // rb = 16-row blocks per wave (1 or 2).  dtype: 0 = f32, 1 = bf16.

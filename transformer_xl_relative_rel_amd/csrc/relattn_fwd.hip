@@ -225,7 +225,7 @@ struct Kernel {
         const int per = a.nsplit;
         const int qb_rank = slot / (G * per);
         const int r2 = slot - qb_rank * G * per;
-        const int bh = xg * G + r2 / per;
+        const int bh = a.remap ? xcd_pair(a, xg, r2 / per) : r2 / per;
         const int split = r2 % per;
         const int qb = a.nqb - 1 - qb_rank;   // the longest query blocks start first
         const int b = bh / a.H, h = bh - b * a.H;

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     const int per = a.nsplit;
     const int grp = slot / (G * per);
     const int r2 = slot - grp * G * per;
-    const int bh = xg * G + r2 / per;
+    const int bh = a.remap ? xcd_pair(a, xg, r2 / per) : r2 / per;
     const int split = r2 % per;
     const int b = bh / a.H, h = bh - b * a.H;
     const int L = a.L, M = a.M, K = a.K;

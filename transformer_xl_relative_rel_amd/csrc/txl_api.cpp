@@ -251,7 +251,7 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     a.nqb = p.nqb;
     a.nsplit = p.nsplit;
     a.tiles_per_split = p.tps;
-    a.remap = ((d->B * d->H) % 8 == 0) ? 1 : 0;
+    a.remap = (d->H % 8 == 0) ? 2 : ((d->B * d->H) % 8 == 0 ? 1 : 0);
     a.mem_valid = d->mem_valid;
     a.window = d->window;
     hipError_t e = p.stream ? txl::launch_relattn_bf16_stream(a, d->dh, static_cast<hipStream_t>(stream))
