@@ -678,8 +678,20 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     const int psub = wave & 3, bg = wave >> 2;
     const int L = a.L, K = a.K;
     const int nkb = (K + BK - 1) / BK;
-    const int h = blockIdx.x / nkb;
-    const int p0 = BK * (blockIdx.x - h * nkb);
+    // Workgroup w runs on XCD w mod 8.  With H a multiple of 8 every column
+    // block of head h runs on XCD h mod 8, so the head's qv rows, which all its
+    // blocks read, are fetched into one L2.
+    int h, kbi;
+    if ((a.H & 7) == 0) {
+        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int hh = slot / nkb;
+        kbi = slot - hh * nkb;
+        h = hh * 8 + x;
+    } else {
+        h = blockIdx.x / nkb;
+        kbi = blockIdx.x - h * nkb;
+    }
+    const int p0 = BK * kbi;
     const int tg = psub * 64 + lane;              // thread within the batch group
     const int lrow = tg / CPR, lpos = tg & (CPR - 1);   // rows lrow and lrow + 32 of a step
     const int lc0 = lpos ^ swz(lrow), lc1 = lpos ^ swz(lrow + 32);
