@@ -114,29 +114,43 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dq (and G, and the bias partial sums)
+// dq (and the bias partial sums) from the score gradients G that dkv stored
 
-constexpr int QW = 8;               // waves per workgroup
+constexpr int QW = 4;               // waves per workgroup
 constexpr int QROWS = 16 * QW;      // queries per workgroup
 constexpr int QTHR = 64 * QW;
+constexpr int QLPT = TILE_CH / QTHR;   // 16-byte loads per thread per tile
 constexpr int RQ = 4;               // r ring quarters: three in use, one loading
-static_assert(TILE_CH == QTHR, "one 16-byte load per thread per tile");
+static_assert(QLPT * QTHR == TILE_CH, "whole tiles per load round");
 static_assert(QROWS - 16 + 16 * NBT <= 64 * (RQ - 1), "a tile's bands fit in three ring quarters");
 
-// Skew row of query n: row n uses columns min(n + 1, 16) .. n + 80, and rows
-// start 80 to 92 floats apart, so one row's used columns never meet another's.
-// The starts keep the one-word band stores (32 lanes over 32 banks per
-// cycle) and the 16-byte dS stores (8 lanes over 32 banks per cycle) free of
-// bank conflicts; starts are multiples of 4, so 16-byte accesses are aligned.
-__device__ __forceinline__ int skew_row(int n) { return 168 * (n >> 1) - 4 * ((n >> 2) & 1) + 80 * (n & 1); }
-constexpr int SKEW = 1252 + 96;   // skew_row(15) + 96 floats per wave
+// G staging: the G window of one wave and one key tile is 16 rows x GCOL
+// columns starting at an 8-aligned column; row n at 16-byte chunk GRC n.
+constexpr int GCOL = 88;            // band rows 0..79 plus up to 7 columns of alignment slack
+constexpr int GRC = GCOL / 8;       // 16-byte chunks per staged row
+constexpr int GLD = (16 * GRC + 63) / 64;   // staging loads per lane
+constexpr int GBUF = GLD * 1024;    // bytes per wave and buffer
+
+// keep mask of one word (two bf16): element e0 and e0 + 1 kept iff their key lies in [lo, hi]
+__device__ __forceinline__ uint32_t keep2(int j, int lo, int hi)
+{
+    return ((j >= lo && j <= hi) ? 0x0000ffffu : 0u) | ((j + 1 >= lo && j + 1 <= hi) ? 0xffff0000u : 0u);
+}
+// Four consecutive bf16 of a staged row starting at element e (e >= 0): three
+// aligned words, shifted by one element when e is odd.
+__device__ __forceinline__ u32x2 gquad(const TXL_LDS_AS char *row, int e)
+{
+    const TXL_LDS_AS uint32_t *w = (const TXL_LDS_AS uint32_t *)(row + (e >> 1) * 4);
+    const uint32_t sh = (uint32_t)(e & 1) * 2;
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    return u32x2{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh)};
+}
 
 __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sr[RQ][TILE_CH];
-    __shared__ __attribute__((aligned(16))) float sskew[QW][SKEW];
+    __shared__ __attribute__((aligned(16))) char sgw[2][QW][GBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,216 +171,164 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     const int kt1 = min((min(i0 + QROWS - 1, L - 1) + M) / BK + 1, kt0 + a.tps);
     const int ntile_w = i0w < L ? (min(i0w + 15, L - 1) + M) / BK + 1 : 0;
 
-    // per-lane query operands and row constants
-    const int iqc = qok ? iq : 0;
-    const bf16x8 zero8 = {};
-    bf16x8 qu[NKK], qv[NKK], dof[NKK];
-    {
-        const uint16_t *qur = a.qu + ((int64_t)bh * L + iqc) * DH;
-        const uint16_t *qvr = a.qv + ((int64_t)bh * L + iqc) * DH;
-        const uint16_t *dor = static_cast<const uint16_t *>(a.dout) + b * a.os[0] + h * a.os[1] + (int64_t)iqc * a.os[2];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qur + 32 * kk + 8 * g);
-            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(qvr + 32 * kk + 8 * g);
-            const bf16x8 z = *reinterpret_cast<const bf16x8 *>(dor + 32 * kk + 8 * g);
-            qu[kk] = qok ? x : zero8;
-            qv[kk] = qok ? y : zero8;
-            dof[kk] = qok ? z : zero8;
-        }
-    }
-    const float nlse = qok ? -a.lse2[(int64_t)bh * L + iq] : -INFINITY;
-    const float nD = qok ? -a.dd[(int64_t)bh * L + iq] : 0.f;
+    // keys j with kmem <= j <= iq + M have a stored dS (dkv skips key blocks
+    // that lie wholly below the valid memory)
     int kmem_abs = 0;
     if (a.mem_valid) {
         int mv = a.mem_valid[b];
         mv = mv < 0 ? 0 : (mv > M ? M : mv);
         kmem_abs = M - mv;
     }
-    const int win = a.window;
+    const int jhi = qok ? iq + M : -1;
 
-    // direct loads: thread tid moves chunk tid of each 64-row tile
+    // G rows of the head (the (b, h) slab; rows past L and offsets past the
+    // slab read zeros).  Column L-16-i0w+j0+cc of every row is band row cc of
+    // key tile j0; the staged window starts at the 8-aligned column below it.
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.g + (int64_t)bh * L * a.kp, (uint32_t)((int64_t)L * a.kp * 2));
+    const int pcol0 = L - 16 - i0w;
+    const uint32_t sg_base = __builtin_amdgcn_readfirstlane(lds_addr(&sgw[0][wave][0]));
+    auto stage_g = [&](int kt) {
+        const int cs = (pcol0 + kt * BK) & ~7;     // may be negative: those columns are masked
+        const uint32_t boff = (uint32_t)(kt & 1) * (QW * GBUF);
+#pragma unroll
+        for (int e = 0; e < GLD; ++e) {
+            const int q = lane + 64 * e;           // chunk q: row q / GRC, chunk q % GRC
+            const int row = q / GRC, chk = q - row * GRC;
+            const uint32_t goff = (uint32_t)(i0w + row) * (uint32_t)a.kp * 2 + (uint32_t)((cs + 8 * chk) * 2);
+            load_lds16(grs, goff, sg_base + boff + (uint32_t)e * 1024);
+        }
+    };
+
+    // direct loads: thread tid moves chunks tid + QTHR e of each 64-row tile
+    // (rows tid / 8 + (QTHR / 8) e; the swizzle is the same for rows 16 apart)
     const int lrow = tid / CPR;
     const int lch = ((tid & (CPR - 1)) ^ swz(lrow)) * 16;
     const uint16_t *kp = static_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
-    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + b * a.vs[0] + h * a.vs[1];
     const uint16_t *rp = static_cast<const uint16_t *>(a.r) + h * a.rs[0];
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
-    const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
+    const int krow_b = (int)a.ks[2] * 2, rrow_b = (int)a.rs[1] * 2;
     const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][wave * 64]));
-    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][wave * 64]));
     const uint32_t sr_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0][wave * 64]));
     // ring row x holds r row cb + x; wave w's band tile bt of key tile kt starts at
     // ring row xw + 64 kt + 16 bt (band row cc of query n <-> key cc + n - 15)
     const int cb = L - QROWS - i0;
     const int xw = QROWS - 16 - 16 * wave;
-    auto load_kv = [&](int kt) {
+    auto load_k = [&](int kt) {
         const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
-        const int row = kt * BK + lrow;
-        load_lds16(krs, (uint32_t)(row * krow_b + lch), sk_base + boff);
-        load_lds16(vrs, (uint32_t)(row * vrow_b + lch), sv_base + boff);
+#pragma unroll
+        for (int e = 0; e < QLPT; ++e)
+            load_lds16(krs, (uint32_t)((kt * BK + lrow + (QTHR / CPR) * e) * krow_b + lch),
+                       sk_base + boff + (uint32_t)e * (QTHR * 16));
     };
     auto load_r_quarter = [&](int q) {
         const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
-        load_lds16(rrs, (uint32_t)((cb + 64 * q + lrow) * rrow_b + lch), sr_base + qoff);
+#pragma unroll
+        for (int e = 0; e < QLPT; ++e)
+            load_lds16(rrs, (uint32_t)((cb + 64 * q + lrow + (QTHR / CPR) * e) * rrow_b + lch),
+                       sr_base + qoff + (uint32_t)e * (QTHR * 16));
     };
 
     f32x4 dqu[NDT], dqv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqu[dt] = dqv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the G window of a tile is staged in LDS one tile ahead (two buffers)
     if (kt0 < kt1) {
-        load_kv(kt0);
+        load_k(kt0);
 #pragma unroll
         for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
+        if (kt0 < ntile_w) stage_g(kt0);
     }
-    float *skw = sskew[wave];
-    const int rowb = skew_row(n);
-    uint16_t *grow = a.g + ((int64_t)bh * L + iqc) * a.kp;
-
-    // The G row of a tile is stored at the start of the next iteration, right
-    // after that iteration's loads, so that the wait for the next tile's loads
-    // does not also wait for stores issued just before it.
-    f32x4 gprev[NT];
-    // Every column a tile can produce, L-1-i+j for j up to the wave's last key
-    // tile end, is below K + 78 <= kp, so rows are stored whole: columns >= K
-    // (keys past i + M, dS = 0) land in the row's padding, which dr ignores.
-    auto store_g = [&](int kt) {
-        if (!qok) return;
-        uint16_t *gp = grow + (L - 1 - iq + kt * BK + 4 * g);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) gp[16 * tt + v] = bf16_bits(gprev[tt][v]);
-    };
     // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
-    const int rlo0 = row_lane_off(0, g, n), rlo1 = row_lane_off(1, g, n);
     int trl[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
-    // Skew columns of row n that the position part reads but no key of the
-    // tile fills: [n + 1, 16) and [80, n + 81), 16 per row; lane (g, n) zeroes
-    // four of them after the band values there have served their purpose.
-    int zoff[4];
+    // Band rows of query n outside its own 64 keys (cc < 15 - n or cc > 78 - n)
+    // belong to the neighbouring tiles: fixed keep masks for k-steps 0 and 2.
+    uint32_t pm0[2][2], pm2[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int k = 4 * g + e;
-        zoff[e] = rowb + (k < 15 - n ? n + 1 + k : 80 + k - (15 - n));
-    }
-    for (int kt = kt0; kt < kt1; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 < kt1) {
-            load_kv(kt + 1);
-            load_r_quarter(kt + RQ - 1);
-        }
-        if (kt > kt0 && kt - 1 < ntile_w) store_g(kt - 1);
-        if (kt >= ntile_w) continue;
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) pm0[hf][w] = keep2(16 * hf + 4 * g + 2 * w, 15 - n, 78 - n);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) pm2[w] = keep2(64 + 4 * g + 2 * w, 15 - n, 78 - n);
+
+    auto tile = [&](int kt) {
         const int j0 = kt * BK;
         const TXL_LDS_AS char *tk = lds_bytes(sk[kt & 1]);
-        const TXL_LDS_AS char *tv = lds_bytes(sv[kt & 1]);
+        // this lane's staged row; element e of it is column cs + e
+        const int cs = (pcol0 + j0) & ~7;
+        const TXL_LDS_AS char *grow = (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)&sgw[kt & 1][wave][0] + n * (GRC * 16);
+        const int ec = (L - 1 - iq + j0) - cs;   // content: key j0 + k at element ec + k (>= 15 - n)
+        const int ep = (pcol0 + j0) - cs;         // position: band row cc at element ep + cc (0..7)
         auto ring_blk = [&](int x0) {   // 16-row block of ring rows x0 .. x0 + 15 (x0 % 16 == 0)
             return lds_bytes(sr[(x0 >> 6) & (RQ - 1)]) + (x0 & 63) * (CPR * 16);
         };
-
-        // band: T^T = R_band . (c (q + vb))^T - lse2, masked band rows at -inf;
-        // all fragment reads first, then the MFMAs
-        const int thi = M + i0w - j0 + 15;
-        const int tlo = win > 0 ? M + 1 - win + i0w - j0 + 15 : -(1 << 30);
-        f32x4 acc[NBT];
-        auto band = [&](auto MASKED) {
-            bf16x8 rf[NBT][2];
+        // keys outside [kmem, iq + M] have no stored dS: masked on the tiles that reach them
+        const bool edge = j0 + BK - 1 > i0w + M || j0 < kmem_abs || !qok;
+        // content part: dq^T += K^T . dS^T
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) {
-                const TXL_LDS_AS char *rb = ring_blk(xw + 64 * kt + 16 * bt);
-                rf[bt][0] = row_frag_at(rb, rlo0);
-                rf[bt][1] = row_frag_at(rb, rlo1);
-            }
+        for (int ch = 0; ch < 2; ++ch) {
+            u32x2 lo = gquad(grow, ec + 32 * ch + 4 * g), hi = gquad(grow, ec + 32 * ch + 16 + 4 * g);
+            if (edge) {
+                const int jl = j0 + 32 * ch + 4 * g;
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) {
-                f32x4 cin = {nlse, nlse, nlse, nlse};
-                if constexpr (decltype(MASKED)::value) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int row = 16 * bt + 4 * g + v;
-                        if (row > thi || row < tlo) cin[v] = -INFINITY;
-                    }
+                for (int w = 0; w < 2; ++w) {
+                    lo[w] &= keep2(jl + 2 * w, kmem_abs, jhi);
+                    hi[w] &= keep2(jl + 16 + 2 * w, kmem_abs, jhi);
                 }
-                acc[bt] = mfma(rf[bt][0], qv[0], cin);
-                acc[bt] = mfma(rf[bt][1], qv[1], acc[bt]);
             }
-        };
-        if (thi < 16 * NBT - 1 || tlo > 0) band(std::true_type{});
-        else band(std::false_type{});
-        lds_order();
-#pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) lds_store4(skw + rowb + 16 * bt + 4 * g + n + 1, acc[bt]);
-        lds_order();
-        // content on top of the skewed band: log2-domain score minus lse
-        f32x4 sc[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) sc[tt] = *reinterpret_cast<const f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g);
-        lds_order();
-        if (kmem_abs > j0) {
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (j0 + 16 * tt + 4 * g + v < kmem_abs) sc[tt][v] = -INFINITY;
-        }
-        f32x4 gs[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 s = mfma(row_frag_at(tk + tt * 16 * CPR * 16, rlo0), qu[0], sc[tt]);
-            s = mfma(row_frag_at(tk + tt * 16 * CPR * 16, rlo1), qu[1], s);
-            f32x4 dp = {nD, nD, nD, nD};
-            dp = mfma(row_frag_at(tv + tt * 16 * CPR * 16, rlo0), dof[0], dp);
-            dp = mfma(row_frag_at(tv + tt * 16 * CPR * 16, rlo1), dof[1], dp);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) gs[tt][v] = __builtin_amdgcn_exp2f(s[v]) * dp[v];
-        }
-        // content part of dq: dq^T += K^T . dS^T
-#pragma unroll
-        for (int ch = 0; ch < NT / 2; ++ch) {
-            const bf16x8 gf = pack8(gs[2 * ch], gs[2 * ch + 1]);
+            const bf16x8 gf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) dqu[dt] = mfma(col_frag_at(tk + ch * 32 * CPR * 16, trl[dt]), gf, dqu[dt]);
         }
-        // dS into the skew row at key positions (columns 16..79), zeros in the
-        // row's other read positions; read back at band positions
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<f32x4 *>(skw + rowb + 16 + 16 * tt + 4 * g) = gs[tt];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) skw[zoff[e]] = 0.f;
-        lds_order();
         // position part: dq^T += R_band^T . G^T over band rows 0..79 in three
-        // k-steps (band rows 32 ks + {4g + e, 16 + 4g + e}; rows >= 80 are zero)
+        // k-steps (band rows 32 ks + {4 g + e, 16 + 4 g + e}; rows >= 80 are zero)
 #pragma unroll
         for (int ks = 0; ks < 3; ++ks) {
-            f32x8 gv;
+            u32x2 lo = gquad(grow, ep + 32 * ks + 4 * g);
+            u32x2 hi = ks < 2 ? gquad(grow, ep + 32 * ks + 16 + 4 * g) : u32x2{0u, 0u};
+            if (ks == 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                gv[e] = skw[rowb + 32 * ks + 4 * g + e + n + 1];
-                gv[4 + e] = ks < 2 ? skw[rowb + 32 * ks + 16 + 4 * g + e + n + 1] : 0.f;
+                for (int w = 0; w < 2; ++w) {
+                    lo[w] &= pm0[0][w];
+                    hi[w] &= pm0[1][w];
+                }
+            } else if (ks == 2) {
+#pragma unroll
+                for (int w = 0; w < 2; ++w) lo[w] &= pm2[w];
             }
-            const bf16x8 gt = __builtin_convertvector(gv, bf16x8);
+            if (edge) {
+                // band row cc of query n is key j0 + cc + n - 15
+                const int jl = j0 + 32 * ks + 4 * g + n - 15;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    lo[w] &= keep2(jl + 2 * w, kmem_abs, jhi);
+                    hi[w] &= keep2(jl + 16 + 2 * w, kmem_abs, jhi);
+                }
+            }
+            const bf16x8 gt = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             const TXL_LDS_AS char *blo = ring_blk(xw + 64 * kt + 32 * ks);
             const TXL_LDS_AS char *bhi = ring_blk(xw + 64 * kt + 32 * ks + 16);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const u32x2 lo = tr_half(blo, trl[dt]);
-                const u32x2 hi = ks < 2 ? tr_half(bhi, trl[dt]) : u32x2{0u, 0u};
-                dqv[dt] = mfma(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), gt, dqv[dt]);
+                const u32x2 rlo = tr_half(blo, trl[dt]);
+                const u32x2 rhi = ks < 2 ? tr_half(bhi, trl[dt]) : u32x2{0u, 0u};
+                dqv[dt] = mfma(__builtin_bit_cast(bf16x8, u32x4{rlo[0], rlo[1], rhi[0], rhi[1]}), gt, dqv[dt]);
             }
         }
-        lds_order();
-        // G row of this query (column L-1-i+j for key j), stored next iteration
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) gprev[tt] = gs[tt];
+    };
+    for (int kt = kt0; kt < kt1; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < kt1) {
+            load_k(kt + 1);
+            load_r_quarter(kt + RQ - 1);
+            if (kt + 1 < ntile_w) stage_g(kt + 1);
+        }
+        if (kt < ntile_w) tile(kt);
     }
-    if (kt1 > kt0 && kt1 - 1 < ntile_w) store_g(kt1 - 1);
 
     const float scale = a.scale;
     if (qok && a.nsplit == 1) {
@@ -463,6 +425,7 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         kmem_abs = M - mv;
     }
     const int win = a.window;
+    uint16_t *grow = a.g + (int64_t)bh * L * a.kp;
     // queries below j0 - M see no key of the block; a block entirely below the
     // valid memory is seen by nobody
     int ibeg = j0 - M > 0 ? ((j0 - M) / QS) * QS : 0;
@@ -621,6 +584,18 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
                 }
             }
         }
+        // dS of the visible pairs (j <= i + M) to G[i][L-1-i+j] for dq and dr;
+        // masked pairs inside the step store zeros
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int kx = 0; kx < 2; ++kx)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = i0 + 16 * x + 4 * g + v;
+                    const int j = jw0 + 16 * kx + n;
+                    if (i < L && j <= i + M) grow[(int64_t)i * a.kp + (L - 1 - i + j)] = bf16_bits(gs[x][kx][v]);
+                }
         bf16x8 pb[2], gb[2];
 #pragma unroll
         for (int kx = 0; kx < 2; ++kx) {
@@ -701,7 +676,8 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     const int nsteps = ((a.B + RG - 1) / RG) * nch;   // same count for every group
 
     // A fetch only issues loads; the mask of never-written columns (below
-    // L-1-i: keys before the first; at or past K) is computed from the indices
+    // L-1-i + kmem: keys before the first valid one; at or past K: keys past
+    // i + M) is computed from the indices
     // and applied when the data is written to LDS, so the loads stay in flight.
     struct Fetch {
         u32x4 g[2], q[2];
@@ -715,7 +691,14 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
             const int64_t bh = (int64_t)b * a.H + h;
             gr = *reinterpret_cast<const u32x4 *>(a.g + (bh * L + i) * a.kp + p0 + 8 * lc);
             qr = *reinterpret_cast<const u32x4 *>(a.qv + (bh * L + i) * DH + 8 * lc);
-            const int cmin = L - 1 - i;
+            // keys below the valid memory were not stored when their whole key block is hidden
+            int kmem = 0;
+            if (a.mem_valid) {
+                int mv = a.mem_valid[b];
+                mv = mv < 0 ? 0 : (mv > a.M ? a.M : mv);
+                kmem = a.M - mv;
+            }
+            const int cmin = L - 1 - i + kmem;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int col = p0 + 8 * lc + e;
@@ -824,8 +807,9 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(RelAttnBwdArgs a)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Row stride of the stored score gradients: columns reach K + 77 (see the dq
-// kernel's G stores), rounded up to 64.
+// Row stride of the stored score gradients: stored columns stay below K; the
+// dq kernel's operand loads reach column K + 70 (tiles past a query's last
+// visible key, masked), rounded up to 64.
 int g_row_stride(int K) { return ((K + 78 + BK - 1) / BK) * BK; }
 
 // Key splits of the dq kernel: enough workgroups for one per CU (the kernel's
@@ -892,12 +876,12 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     const int64_t rows = (int64_t)a.B * a.H * a.L;
     const int BH = a.B * a.H;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
+    // dkv stores the score gradients G that dq and dr read
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS) * a.nsplit)), dim3(QTHR), 0, s, a);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(bwd_dq_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
-    // dr right after dq, while the score gradients dq stored are freshest in the caches
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);
     return hipGetLastError();
 }

@@ -274,6 +274,10 @@ static txl_status check_bwd(const txl_relattn_desc *d)
     const int64_t row = std::max(std::max(d->k_stride[2], d->v_stride[2]), d->r_stride[1]);
     if ((K + 64) * row * 2 >= ((int64_t)1 << 31) || ((int64_t)d->L + 32) * d->o_stride[2] * 2 >= ((int64_t)1 << 31))
         return fail(TXL_ERR_UNSUPPORTED, "one head's rows span 2 GiB or more");
+    // one head's stored score gradients (L rows of the workspace's G rows)
+    const int64_t kp = ((K + 78 + 63) / 64) * 64;
+    if ((int64_t)d->L * kp * 2 >= ((int64_t)1 << 31))
+        return fail(TXL_ERR_UNSUPPORTED, "one head's score gradients span 2 GiB or more");
     return TXL_OK;
 }
 
