@@ -425,7 +425,8 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         kmem_abs = M - mv;
     }
     const int win = a.window;
-    uint16_t *grow = a.g + (int64_t)bh * L * a.kp;
+    const __amdgpu_buffer_rsrc_t gws = make_rsrc(a.g + (int64_t)bh * L * a.kp, (uint32_t)((int64_t)L * a.kp * 2));
+    const int gstep = __builtin_amdgcn_readfirstlane(2 * (a.kp - 1));   // bytes from (i, c) to (i + 1, c - 1)
     // queries below j0 - M see no key of the block; a block entirely below the
     // valid memory is seen by nobody
     int ibeg = j0 - M > 0 ? ((j0 - M) / QS) * QS : 0;
@@ -584,18 +585,28 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
                 }
             }
         }
-        // dS of the visible pairs (j <= i + M) to G[i][L-1-i+j] for dq and dr;
-        // masked pairs inside the step store zeros
+        // dS of the visible pairs (i < L, j <= i + M) to G[i][L-1-i+j] for dq and
+        // dr (masked pairs inside the step store zeros).  Element (i, L-1-i+j)
+        // sits at byte 2 (i (kp - 1) + L - 1 + j) of the (b, h) slab: one lane
+        // offset per (x, kx), the row step v in the scalar offset; stores of
+        // invisible pairs go past the slab and are dropped.
+        {
+            const bool gfull = jw0 + KPW - 1 <= i0 + M && i0 + QS <= L;
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int kx = 0; kx < 2; ++kx)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = i0 + 16 * x + 4 * g + v;
+                for (int kx = 0; kx < 2; ++kx) {
+                    const int ib = i0 + 16 * x + 4 * g;
                     const int j = jw0 + 16 * kx + n;
-                    if (i < L && j <= i + M) grow[(int64_t)i * a.kp + (L - 1 - i + j)] = bf16_bits(gs[x][kx][v]);
+                    const uint32_t vo = (uint32_t)(ib * (a.kp - 1) + L - 1 + j) * 2;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        uint32_t off = vo;
+                        if (!gfull && (ib + v >= L || j > ib + v + M)) off = 0x80000000u;
+                        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(gs[x][kx][v]), gws, (int)off, v * gstep, 0);
+                    }
                 }
+        }
         bf16x8 pb[2], gb[2];
 #pragma unroll
         for (int kx = 0; kx < 2; ++kx) {
