@@ -16,19 +16,9 @@
 //   dr_c = scale sum over b and (i, j) with L-1-i+j = c of dS_ij (q_i + vb)
 //   du = sum over b, i of the k part of dq_i, dvb = the same of its r part.
 //
-// Kernels (one stream, in the order prep, dq, dr, dkv, bias):
+// Kernels (one stream, in the order prep, dkv, dq, dr, bias):
 //   prep : c (q + u) and c (q + vb) rounded to bf16 exactly as the forward
 //          forms its query operands (c = scale log2 e), D_i, lse in log2 units.
-//   dq   : one wave per 16 queries, 8 waves per workgroup, keys in tiles of
-//          64, transposed like the forward (keys on MFMA rows, queries on
-//          lanes).  Recomputes p from lse (band MFMA + LDS skew rows + content
-//          MFMA, as the forward), dP^T = V . dout^T, dS; then
-//          dq^T += K^T . dS^T (K^T through the transposing LDS read) and, for
-//          the position part, writes dS into the skew row at key positions and
-//          reads it back at band positions: dq^T += R_band^T . G^T with
-//          G[i][c] = dS[i][c - (L-1-i)].  G is also stored to the workspace
-//          (row i, column c) for dr, and per-block sums of both dq parts go
-//          to the workspace for du and dvb.
 //   dkv  : one workgroup per 128 keys (4 waves of 32 keys), queries in steps
 //          of 32, untransposed (queries on MFMA rows, keys on lanes).  The band
 //          T = c (q + vb) . R^T of the step's 32 queries and the 160 r rows
@@ -38,9 +28,16 @@
 //          dv^T += dout^T . P and dk^T += (c (q + u))^T . dS (operands of
 //          the step's query tiles through the transposing LDS read; P and dS
 //          pass from the score MFMA's result layout to the operand layout
-//          without data movement).
-//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r),
-//          launched right after dq.
+//          without data movement).  It also stores dS of the visible pairs as
+//          G[i][L-1-i+j] (bf16) to the workspace.
+//   dq   : one wave per 16 queries, 4 waves per workgroup, keys in tiles of
+//          64, transposed (head columns on MFMA rows, queries on lanes).  The
+//          wave's G window of a tile (16 rows x 88 columns) is staged in LDS
+//          with direct loads; dq^T += K^T . dS^T reads dS at key positions
+//          (row i shifted by L-1-i: aligned words and a byte shift), and
+//          dq^T += R_band^T . G^T reads the same rows at band positions.  Per
+//          16-query sums of both parts go to the workspace for du and dvb.
+//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r).
 //   bias : du, dvb from the per-block sums, in a fixed order.
 // No atomics: every output element has one writer and a fixed summation
 // order, so results are bitwise reproducible.
