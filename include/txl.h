@@ -133,7 +133,7 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *desc, const void *q, const vo
 
 /* Bytes of device workspace txl_relattn_bwd needs for `desc` (always > 0:
  * the prepared query operands, row constants and one bf16 [B][H][L][K']
- * buffer of score gradients, K' = K rounded up to 64).  *bytes is written on
+ * buffer of score gradients, K' = K + 78 rounded up to 64).  *bytes is written on
  * success; the same errors as txl_relattn_bwd for an unsupported desc. */
 txl_status txl_relattn_bwd_workspace_size(const txl_relattn_desc *desc, size_t *bytes);
 
@@ -161,7 +161,8 @@ txl_status txl_relattn_bwd_workspace_size(const txl_relattn_desc *desc, size_t *
  *   desc->k_stride and desc->v_stride, all of `dtype`;
  *   dr [H][K][dh] fp32 contiguous, du and dvb [H][dh] fp32 contiguous.
  * Supported: dtype TXL_BF16 with dh = 64 (else TXL_ERR_UNSUPPORTED), one
- * head's rows within 2 GiB.  Workspace: txl_relattn_bwd_workspace_size()
+ * head's rows and one head's score gradients (L x K' bf16) each within
+ * 2 GiB.  Workspace: txl_relattn_bwd_workspace_size()
  * bytes, 256-byte aligned.  No output may overlap an input, another output or
  * the workspace (TXL_ERR_ALIAS).  Results are bitwise reproducible (fixed
  * summation orders, no atomics).  desc->splits is ignored. */
