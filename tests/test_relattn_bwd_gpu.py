@@ -53,7 +53,11 @@ def run_gpu(d, window=0, mem_valid=None):
     u, vb = dev(d["u"], torch.float32), dev(d["vb"], torch.float32)
     mv = None if mem_valid is None else torch.tensor(mem_valid, dtype=torch.int32, device=DEV)
     out, lse = txl.relattn_fwd(q, k, v, r, u, vb, want_lse=True, window=window, mem_valid=mv)
-    grads = txl.relattn_bwd(q, k, v, r, u, vb, out, lse, dout, window=window, mem_valid=mv)
+    # workspace filled with 0xff bytes (bf16 and fp32 NaN): a read of anything the
+    # kernels did not write first shows up as a non-finite gradient
+    nbytes = txl.relattn_bwd_workspace_size(q, k, v, r, out, dout, window=window, mem_valid=mv)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    grads = txl.relattn_bwd(q, k, v, r, u, vb, out, lse, dout, window=window, mem_valid=mv, workspace=ws)
     torch.cuda.synchronize()
     return {n: t.float().cpu().numpy().astype(np.float64) for n, t in zip(NAMES, grads)}
 
@@ -86,6 +90,8 @@ CASES = [
     (2, 2, 40, 24, 0.5, 0, [5, 24]),
     (2, 1, 130, 70, 0.5, 50, [0, 33]),
     (9, 2, 40, 30, 0.5, 0, None),          # batch rows not a multiple of the dr kernel's 4 batch groups
+    (2, 2, 64, 300, 0.5, 0, [20, 300]),    # row 0 hides keys 0..279: whole 128-key blocks never stored
+    (1, 2, 70, 260, 0.5, 90, [3]),         # window and hidden blocks together
 ]
 
 
