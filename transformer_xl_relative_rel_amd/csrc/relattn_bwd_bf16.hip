@@ -820,8 +820,8 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // visible key, masked), rounded up to 64.
 int g_row_stride(int K) { return ((K + 78 + BK - 1) / BK) * BK; }
 
-// Key splits of the dq kernel: enough workgroups for one per CU (the kernel's
-// LDS allows one), each split at least one key tile.
+// Key splits of the dq kernel: at least 256 workgroups (one per CU; the
+// kernel's 72 KB of LDS allow two), each split at least one key tile.
 void dq_split_plan(int B, int H, int L, int M, int &nsplit, int &tps)
 {
     const int nqb = (L + QROWS - 1) / QROWS;
