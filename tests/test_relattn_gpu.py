@@ -94,6 +94,8 @@ BF16_CASES = [
     (1, 2, 1, 0, 64, 0), (2, 2, 19, 5, 32, 0), (1, 4, 128, 128, 64, 0), (2, 8, 200, 77, 64, 0),
     (1, 2, 96, 33, 128, 0), (2, 8, 256, 256, 64, 0), (1, 16, 128, 640, 64, 0), (1, 2, 70, 300, 64, 4),
     (4, 8, 256, 128, 64, 1),
+    # B*H a multiple of 8 but H not: the XCD order by blocks of (b, h) pairs
+    (4, 2, 160, 96, 64, 0), (2, 12, 150, 64, 64, 0),
 ]
 
 
