@@ -162,6 +162,29 @@ struct Blk {
     int kmem;   // keys below kmem (tile-relative) are masked (per-row memory validity)
 };
 
+// Byte offsets of this lane's part of every LDS fragment access, fixed for the
+// whole key loop: the tile, the 32-row half, the sub-tile and the ring slot add
+// wave-uniform amounts (immediate offsets or one scalar base per buffer).
+struct LaneOff {
+    int k[NKK];     // K and r fragments: row n of a 16-row block, chunk (4 kk + g) under the swizzle
+    int v[NDT];     // V^T: rows 4 g + n / 4 (+ 16 for the upper half, + 32 per chunk), column block dt
+    int sst, sld;   // skew row: store at column 4 g + n + 1, load at column 16 + 4 g (floats)
+};
+
+__device__ __forceinline__ LaneOff lane_offsets(int g, int n)
+{
+    LaneOff o;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) o.k[kk] = (n * CPR + ((4 * kk + g) ^ swz_k(n))) * 16;
+    const int row0 = 4 * g + (n >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        o.v[dt] = (row0 * CPR + ((2 * dt + ((n >> 1) & 1)) ^ swz_v(row0))) * 16 + 8 * (n & 1);
+    o.sst = skew_row(n) + 4 * g + n + 1;
+    o.sld = skew_row(n) + 16 + 4 * g;
+    return o;
+}
+
 struct Tile {
     const u32x4 *sk, *sv, *sr;
     float *skw;         // this wave's skew buffer
@@ -175,41 +198,34 @@ struct Tile {
 // MASKED: some key of the run is masked on this tile (band rows or key
 // columns); otherwise every band row starts at -m.
 template <bool LOWER, bool MASKED>
-__device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, int n)
+__device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, const LaneOff &lo)
 {
-    // Lane ids made opaque here, so that the lane parts of fragment addresses
-    // and mask bounds are recomputed per tile (a few adds) instead of being
-    // hoisted out of the tile loop, where they would stay live in registers
-    // (and spill) across the whole loop.
-    asm volatile("" : "+v"(g), "+v"(n));
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-    // Lane part of a fragment read: row n of a 16-row group, chunk (4 kk + g)
-    // under the row swizzle, which only depends on n for rows 16 apart.
-    int lane_ch[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) lane_ch[kk] = n * CPR + ((4 * kk + g) ^ swz_k(n));
     // K fragments (A operands of the content MFMA), shared by the two blocks
     bf16x8 kf[NT][NKK];
+    {
+        const TXL_LDS_AS char *kb = lds_bytes(t.sk);
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            kf[tt][kk] = __builtin_bit_cast(bf16x8, t.sk[16 * tt * CPR + lane_ch[kk]]);
+            for (int kk = 0; kk < NKK; ++kk)
+                kf[tt][kk] = *(const TXL_LDS_AS bf16x8 *)(kb + lo.k[kk] + tt * 16 * CPR * 16);
+    }
     // r fragments of one run: run band tile u holds ring rows offr + 16 u + n.
     // A 16-row band tile never straddles a 64-row quarter (offr is a multiple
     // of 32), so its quarter slot is uniform across the wave.
     bf16x8 rf[NRB][NKK];
     auto load_r = [&]() {
-        const u32x4 *sr = t.sr;
+        const TXL_LDS_AS char *srb = lds_bytes(t.sr);
         const int offr = t.offr;
 #pragma unroll
         for (int u = 0; u < NRB; ++u) {
             const int x0 = offr + 16 * u;   // wave-uniform
-            const int ubase = ((t.kt + (x0 >> 6)) & (RQ - 1)) * TILE_CH + (x0 & 63) * CPR;
+            const int ubase = (((t.kt + (x0 >> 6)) & (RQ - 1)) * TILE_CH + (x0 & 63) * CPR) * 16;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = __builtin_bit_cast(bf16x8, sr[ubase + lane_ch[kk]]);
+            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = *(const TXL_LDS_AS bf16x8 *)(srb + ubase + lo.k[kk]);
         }
     };
     // V^T fragments (A operands of P.V), read through the transposing LDS read
@@ -220,15 +236,12 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         for (int ch = 0; ch < NT / 2; ++ch)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                // lane (g, n) gets V[32 ch + 4 g + e][16 dt + n] (lo) and the rows 16 below (hi)
-                const int row0 = 32 * ch + 4 * g + (n >> 2);
-                const int chunk = 2 * dt + ((n >> 1) & 1);
-                const int off0 = (row0 * CPR + (chunk ^ swz_v(row0))) * 16 + 8 * (n & 1);
-                const int row1 = row0 + 16;
-                const int off1 = (row1 * CPR + (chunk ^ swz_v(row1))) * 16 + 8 * (n & 1);
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off0));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off1));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                // lane (g, n) gets V[32 ch + 4 g + e][16 dt + n] (lo) and the rows 16 below (hi);
+                // the swizzle of rows 32 ch + r and 32 ch + r + 16 is that of row r
+                TXL_LDS_AS char *p0 = vb + lo.v[dt] + ch * 32 * CPR * 16;
+                const i16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)p0);
+                const i16x4 hh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(p0 + 16 * CPR * 16));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, l), h2 = __builtin_bit_cast(u32x2, hh);
                 vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
             }
     };
@@ -268,7 +281,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         lds_order();
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt)   // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
-            lds_store4(skw + skew_row(n) + 16 * bt + 4 * g + n + 1, acc[bt]);
+            lds_store4(skw + lo.sst + 16 * bt, acc[bt]);
         lds_order();
     };
     // B: content MFMA of block x on top of the skewed band values
@@ -278,7 +291,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         f32x4 cin[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + skew_row(n) + 16 + 16 * tt + 4 * g);
+            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + lo.sld + 16 * tt);
         lds_order();
         if (LOWER && MASKED) {
             // keys below kmem are hidden from every query of the block
@@ -496,6 +509,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    const LaneOff lo = lane_offsets(g, n);
     Tile t;
     t.sr = sr[end];
     t.skw = sskew[wave];
@@ -542,7 +556,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
             t.sv = sv[kt & 1];
             t.kt = kt;
             t.first = (kt == kt0);
-            tile_body<LOWER, MASKED>(st, t, bk, g, n);
+            tile_body<LOWER, MASKED>(st, t, bk, g, lo);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
