@@ -166,20 +166,20 @@ struct Blk {
 // whole key loop: the tile, the 32-row half, the sub-tile and the ring slot add
 // wave-uniform amounts (immediate offsets or one scalar base per buffer).
 struct LaneOff {
-    int k[NKK];     // K and r fragments: row n of a 16-row block, chunk (4 kk + g) under the swizzle
-    int v[NDT];     // V^T: rows 4 g + n / 4 (+ 16 for the upper half, + 32 per chunk), column block dt
+    int k0;         // K and r fragments: row n of a 16-row block, chunk g under the swizzle (k-step 1: k0 ^ 64)
+    int v0;         // V^T: rows 4 g + n / 4 (+ 16 for the upper half, + 32 per chunk) of column block 0
+                    // (column block dt: v0 ^ 32 dt)
     int sst, sld;   // skew row: store at column 4 g + n + 1, load at column 16 + 4 g (floats)
 };
 
 __device__ __forceinline__ LaneOff lane_offsets(int g, int n)
 {
     LaneOff o;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) o.k[kk] = (n * CPR + ((4 * kk + g) ^ swz_k(n))) * 16;
+    // chunk (4 kk + g) ^ swz = (g ^ swz) ^ 4 kk: k-step kk flips bit 6 of the byte offset
+    o.k0 = (n * CPR + (g ^ swz_k(n))) * 16;
+    // chunk (2 dt + b) ^ swz = 2 (dt ^ swz / 2) + b (swz even): column block dt flips bits 5-6
     const int row0 = 4 * g + (n >> 2);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-        o.v[dt] = (row0 * CPR + ((2 * dt + ((n >> 1) & 1)) ^ swz_v(row0))) * 16 + 8 * (n & 1);
+    o.v0 = (row0 * CPR + (((n >> 1) & 1) ^ swz_v(row0))) * 16 + 8 * (n & 1);
     o.sst = skew_row(n) + 4 * g + n + 1;
     o.sld = skew_row(n) + 16 + 4 * g;
     return o;
@@ -200,6 +200,11 @@ struct Tile {
 template <bool LOWER, bool MASKED>
 __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, const LaneOff &lo)
 {
+    // The derived offsets (k-step 1, column blocks 1-3) are formed per tile
+    // from the two base offsets, made opaque here so that they are not hoisted
+    // out of the key loop as registers of their own.
+    int k0 = lo.k0, v0 = lo.v0;
+    asm volatile("" : "+v"(k0), "+v"(v0));
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
@@ -211,7 +216,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
-                kf[tt][kk] = *(const TXL_LDS_AS bf16x8 *)(kb + lo.k[kk] + tt * 16 * CPR * 16);
+                kf[tt][kk] = *(const TXL_LDS_AS bf16x8 *)(kb + (k0 ^ (64 * kk)) + tt * 16 * CPR * 16);
     }
     // r fragments of one run: run band tile u holds ring rows offr + 16 u + n.
     // A 16-row band tile never straddles a 64-row quarter (offr is a multiple
@@ -225,7 +230,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
             const int x0 = offr + 16 * u;   // wave-uniform
             const int ubase = (((t.kt + (x0 >> 6)) & (RQ - 1)) * TILE_CH + (x0 & 63) * CPR) * 16;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = *(const TXL_LDS_AS bf16x8 *)(srb + ubase + lo.k[kk]);
+            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = *(const TXL_LDS_AS bf16x8 *)(srb + ubase + (k0 ^ (64 * kk)));
         }
     };
     // V^T fragments (A operands of P.V), read through the transposing LDS read
@@ -238,7 +243,7 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
             for (int dt = 0; dt < NDT; ++dt) {
                 // lane (g, n) gets V[32 ch + 4 g + e][16 dt + n] (lo) and the rows 16 below (hi);
                 // the swizzle of rows 32 ch + r and 32 ch + r + 16 is that of row r
-                TXL_LDS_AS char *p0 = vb + lo.v[dt] + ch * 32 * CPR * 16;
+                TXL_LDS_AS char *p0 = vb + (v0 ^ (32 * dt)) + ch * 32 * CPR * 16;
                 const i16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)p0);
                 const i16x4 hh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(p0 + 16 * CPR * 16));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, l), h2 = __builtin_bit_cast(u32x2, hh);
@@ -579,10 +584,14 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         }
     }
 
-    // ---- epilogue: lane (g, n) holds query n, head columns 16 dt + 4 g + v
+    // ---- epilogue: lane (g, n) holds query n, head columns 16 dt + 4 g + v.
+    // Lane ids made opaque here so that the epilogue's addresses are formed
+    // after the key loop instead of being held (and spilled) across it.
+    int ge = g, ne = n;
+    asm volatile("" : "+v"(ge), "+v"(ne));
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-        const int iq = i0[x] + n;
+        const int iq = i0[x] + ne;
         if (!run_ok || iq >= L) continue;
         const float l = st.lsum[x][0];
         if (a.nsplit == 1) {
@@ -591,14 +600,14 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const bf16x4 yb = __builtin_convertvector(st.o[x][dt] * inv, bf16x4);
-                *reinterpret_cast<u32x2 *>(op + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, yb);
+                *reinterpret_cast<u32x2 *>(op + 16 * dt + 4 * ge) = __builtin_bit_cast(u32x2, yb);
             }
-            if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
+            if (a.lse && ge == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
         } else {
             float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[x][dt];
-            if (g == 0) {
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * ge) = st.o[x][dt];
+            if (ge == 0) {
                 float *pm = a.part_ml + (((int64_t)split * BH + bh) * L + iq) * 2;
                 pm[0] = (l > 0.f) ? st.mref[x] : -INFINITY;   // no visible key in this split
                 pm[1] = l;
