@@ -64,7 +64,10 @@ constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
 constexpr int TILE_CH = BK * CPR;
 constexpr int BLK16B = 16 * CPR * 16;   // bytes of 16 tile rows
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+template <bool B> struct BoolC { static constexpr bool value = B; };   // compile-time flag for generic lambdas
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // ---------------------------------------------------------------------------
@@ -492,6 +495,8 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
     int trl[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) trl[dt] = tr_lane_off(dt, g, n);
+    const bool kmask = jw0 < kmem_abs;                  // keys below the valid memory in this wave
+    const int glane = (4 * g * (a.kp - 1) + n) * 2;      // lane part of a G element's byte offset
     for (int s = 0; s < nsteps; ++s) {
         const int i0 = ibeg + QS * s;
         const int buf = s & 1;
@@ -505,18 +510,18 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         const TXL_LDS_AS char *tqv = lds_bytes(sqv[buf]);
         const TXL_LDS_AS char *tdo = lds_bytes(sdo[buf]);
         // T[i][c] = c (q_i + vb) . r[pw + c] - lse2_i for the step's queries,
-        // with pw the r row of (last query, first key); masked entries -inf
+        // with pw the r row of (last query, first key); masked entries -inf.
+        // Each phase has an unmasked instance for the steps (and waves) that
+        // need no mask, chosen by a wave-uniform branch.
         const int pw = L - 1 - (i0 + QS - 1) + j0;
-        {
+        auto band = [&](auto mtag) {
+            constexpr bool MASKED = decltype(mtag)::value;
             const bf16x8 qa0 = row_frag_at(tqv + s2 * BLK16B, rlo0);
             const bf16x8 qa1 = row_frag_at(tqv + s2 * BLK16B, rlo1);
             f32x4 nl;
 #pragma unroll
             for (int v = 0; v < 4; ++v) nl[v] = -sl2[buf][16 * s2 + 4 * g + v];
-            // masking needed: rows past L, r rows past K-1 (causal) or below K - window
-            const bool qmask = i0 + QS > L;
-            const bool cmask = pw + 16 * (pt0 + TPW) - 1 > K - 1 || (win > 0 && pw + 16 * pt0 < K - win);
-            if (qmask) {
+            if (MASKED) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     if (i0 + 16 * s2 + 4 * g + v >= L) nl[v] = -INFINITY;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 f32x4 cin = nl;
-                if (cmask) {
+                if (MASKED) {
                     const int pc = pw + 16 * (pt0 + u) + n;      // this lane's r row
                     if (pc > K - 1 || (win > 0 && pc < K - win)) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                 }
@@ -545,71 +550,83 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
             for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[u][v];
-        }
+        };
+        // masking needed: rows past L, r rows past K-1 (causal) or below K - window
+        const bool qmask = i0 + QS > L;
+        const bool cmask = pw + 16 * (pt0 + TPW) - 1 > K - 1 || (win > 0 && pw + 16 * pt0 < K - win);
+        if (qmask || cmask) band(BoolC<true>{}); else band(BoolC<false>{});
         __syncthreads();
-        // scores, probabilities and dS of this wave's 32 keys
-        bf16x8 qa[2][NKK], da[2][NKK];
+        // scores, probabilities and dS of this wave's 32 keys; dS of the
+        // visible pairs (i < L, j <= i + M) to G[i][L-1-i+j] for dq and dr
+        // (masked pairs inside the step store zeros).  Element (i, L-1-i+j)
+        // sits at byte 2 (i (kp - 1) + L - 1 + j) of the (b, h) slab.
+        const int gstep_i0 = __builtin_amdgcn_readfirstlane((i0 * (a.kp - 1) + L - 1 + jw0) * 2);
+        bf16x8 pb[2], gb[2];
+        auto scores = [&](auto mtag) {
+            constexpr bool MASKED = decltype(mtag)::value;
+            bf16x8 qa[2][NKK], da[2][NKK];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            qa[x][0] = row_frag_at(tqu + x * BLK16B, rlo0);
-            qa[x][1] = row_frag_at(tqu + x * BLK16B, rlo1);
-            da[x][0] = row_frag_at(tdo + x * BLK16B, rlo0);
-            da[x][1] = row_frag_at(tdo + x * BLK16B, rlo1);
-        }
-        f32x4 p[2][2], gs[2][2];                 // [query sub-tile][key sub-tile]
+            for (int x = 0; x < 2; ++x) {
+                qa[x][0] = row_frag_at(tqu + x * BLK16B, rlo0);
+                qa[x][1] = row_frag_at(tqu + x * BLK16B, rlo1);
+                da[x][0] = row_frag_at(tdo + x * BLK16B, rlo0);
+                da[x][1] = row_frag_at(tdo + x * BLK16B, rlo1);
+            }
+            f32x4 p[2][2], gs[2][2];                 // [query sub-tile][key sub-tile]
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            f32x4 nd;
+            for (int x = 0; x < 2; ++x) {
+                f32x4 nd;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) nd[v] = -sdd[buf][16 * x + 4 * g + v];
+                for (int v = 0; v < 4; ++v) nd[v] = -sdd[buf][16 * x + 4 * g + v];
 #pragma unroll
-            for (int kx = 0; kx < 2; ++kx) {
-                f32x4 cin;
+                for (int kx = 0; kx < 2; ++kx) {
+                    f32x4 cin;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * x + 4 * g + v;
-                    cin[v] = tband[r * TS + KPW * wave + 16 * kx + n - r + QS - 1];
-                }
-                if (jw0 + 16 * kx + n < kmem_abs) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                f32x4 sc = mfma(qa[x][0], kf[kx][0], cin);
-                sc = mfma(qa[x][1], kf[kx][1], sc);
-                f32x4 dp = mfma(da[x][0], vf[kx][0], nd);
-                dp = mfma(da[x][1], vf[kx][1], dp);
+                    for (int v = 0; v < 4; ++v) {
+                        const int r = 16 * x + 4 * g + v;
+                        cin[v] = tband[r * TS + KPW * wave + 16 * kx + n - r + QS - 1];
+                    }
+                    if (MASKED && jw0 + 16 * kx + n < kmem_abs) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                    f32x4 sc = mfma(qa[x][0], kf[kx][0], cin);
+                    sc = mfma(qa[x][1], kf[kx][1], sc);
+                    f32x4 dp = mfma(da[x][0], vf[kx][0], nd);
+                    dp = mfma(da[x][1], vf[kx][1], dp);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    p[x][kx][v] = __builtin_amdgcn_exp2f(sc[v]);
-                    gs[x][kx][v] = p[x][kx][v] * dp[v];
+                    for (int v = 0; v < 4; ++v) {
+                        p[x][kx][v] = __builtin_amdgcn_exp2f(sc[v]);
+                        gs[x][kx][v] = p[x][kx][v] * dp[v];
+                    }
                 }
             }
-        }
-        // dS of the visible pairs (i < L, j <= i + M) to G[i][L-1-i+j] for dq and
-        // dr (masked pairs inside the step store zeros).  Element (i, L-1-i+j)
-        // sits at byte 2 (i (kp - 1) + L - 1 + j) of the (b, h) slab: one lane
-        // offset per (x, kx), the row step v in the scalar offset; stores of
-        // invisible pairs go past the slab and are dropped.
-        {
-            const bool gfull = jw0 + KPW - 1 <= i0 + M && i0 + QS <= L;
+#pragma unroll
+            for (int kx = 0; kx < 2; ++kx) {
+                pb[kx] = pack8(p[0][kx], p[1][kx]);
+                gb[kx] = pack8(gs[0][kx], gs[1][kx]);
+            }
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int kx = 0; kx < 2; ++kx) {
-                    const int ib = i0 + 16 * x + 4 * g;
-                    const int j = jw0 + 16 * kx + n;
-                    const uint32_t vo = (uint32_t)(ib * (a.kp - 1) + L - 1 + j) * 2;
+                for (int kx = 0; kx < 2; ++kx)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        uint32_t off = vo;
-                        if (!gfull && (ib + v >= L || j > ib + v + M)) off = 0x80000000u;
-                        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(gs[x][kx][v]), gws, (int)off, v * gstep, 0);
+                        const uint16_t bits = __builtin_bit_cast(u16x8, gb[kx])[4 * x + v];
+                        if (MASKED) {
+                            // one lane offset per (x, kx), the row step v in the
+                            // scalar offset; invisible pairs go past the slab
+                            const int ib = i0 + 16 * x + 4 * g, j = jw0 + 16 * kx + n;
+                            const uint32_t vo = (uint32_t)(ib * (a.kp - 1) + L - 1 + j) * 2;
+                            const uint32_t off = ib + v >= L || j > ib + v + M ? 0x80000000u : vo;
+                            __builtin_amdgcn_raw_buffer_store_b16(bits, gws, (int)off, v * gstep, 0);
+                        } else {
+                            // lane part in the vector offset, step, row and key
+                            // sub-tile parts uniform
+                            __builtin_amdgcn_raw_buffer_store_b16(bits, gws, glane + 32 * kx,
+                                                                  gstep_i0 + (16 * x + v) * gstep, 0);
+                        }
                     }
-                }
-        }
-        bf16x8 pb[2], gb[2];
-#pragma unroll
-        for (int kx = 0; kx < 2; ++kx) {
-            pb[kx] = pack8(p[0][kx], p[1][kx]);
-            gb[kx] = pack8(gs[0][kx], gs[1][kx]);
-        }
+        };
+        const bool gfull = jw0 + KPW - 1 <= i0 + M && i0 + QS <= L;
+        if (kmask || !gfull) scores(BoolC<true>{}); else scores(BoolC<false>{});
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const bf16x8 dot = col_frag_at(tdo, trl[dt]);
