@@ -199,6 +199,28 @@ txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, 
                                   int dtype, int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new,
                                   void *stream);
 
+/* txl_relattn_fwd and one txl_mem_update in a single call: the attention of
+ * a layer's segment and the Tail_M update of the same layer's memory ([XL]
+ * "Segment-Level Recurrence": the next segment's memory is the last mem_len
+ * rows of [mem; h]).  The two results are exactly those of the two calls
+ * (the copy is bit-exact and independent of the attention); the arguments
+ * and every check are theirs: desc .. workspace_bytes as txl_relattn_fwd,
+ * mem .. M_new as txl_mem_update (B_m batch rows of d_model elements of
+ * dtype_m).  Because the two run concurrently, new_mem must not overlap q,
+ * k, v, r_k, u, vb, out, lse or the workspace, and mem and h must not
+ * overlap out, lse or the workspace (TXL_ERR_ALIAS).  With the bf16
+ * throughput kernel (bf16, dh = 64, not the short-segment streaming case)
+ * the attention kernel's own waves do the copy, 1 KB chunks spread over its
+ * key loop, so the copy rides on HBM bandwidth the attention leaves unused;
+ * otherwise the call launches the attention and then the copy kernel on
+ * `stream`. */
+txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *desc, const void *q, const void *k, const void *v,
+                                      const void *r_k, const float *u, const float *vb, void *out, float *lse,
+                                      void *workspace, size_t workspace_bytes, const void *mem, int M_cur,
+                                      const void *h, int L_h, void *new_mem, int mem_len, int ext_len, int B_m,
+                                      int d_model, int dtype_m, int64_t mem_bs, int64_t h_bs, int64_t new_bs,
+                                      int *M_new, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Decoder layer (relative attention + post-LayerNorm position-wise FF)     */
 /* ------------------------------------------------------------------------ */

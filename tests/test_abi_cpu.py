@@ -136,6 +136,30 @@ def test_mem_update_rejects_bad_arguments():
                                             ctypes.byref(got), vp(0)) == EINVAL
 
 
+def _fwd_mem(d, out=FAKE * 7, lse=0, mem=FAKE * 8, h=FAKE * 9, new=FAKE * 10, M_cur=8, L=8, mem_len=8, B=2, dm=32):
+    vp = ctypes.c_void_p
+    got = ctypes.c_int(-1)
+    return txl.lib().txl_relattn_fwd_mem_update(
+        ctypes.byref(d), vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), vp(FAKE * 6), vp(out),
+        vp(lse), vp(0), 0, vp(mem), M_cur, vp(h), L, vp(new), mem_len, 0, B, dm, txl.BF16, M_cur * dm, L * dm,
+        mem_len * dm, ctypes.byref(got), vp(0))
+
+
+def test_fused_mem_update_rejects_bad_arguments():
+    d = _desc(B=1, H=1, L=8, M=0, dh=64)
+    assert _fwd_mem(d, out=FAKE) == EALIAS              # the attention's own checks
+    assert _fwd_mem(d, mem=0) == EINVAL                 # the memory update's own checks
+    assert _fwd_mem(d, new=FAKE * 8 + 16) == EALIAS     # in place over mem
+    # the two run together: the copy must not write what the attention reads or writes ...
+    assert _fwd_mem(d, new=FAKE * 3 + 64) == EALIAS     # new_mem inside v
+    assert _fwd_mem(d, new=FAKE * 7 + 64) == EALIAS     # new_mem inside out
+    assert _fwd_mem(d, new=FAKE * 5) == EALIAS          # new_mem over u
+    # ... nor read what the attention writes
+    assert _fwd_mem(d, h=FAKE * 7 + 32) == EALIAS       # h inside out
+    assert _fwd_mem(d, lse=FAKE * 8 + 64) == EALIAS     # lse inside mem
+    assert b"overlaps" in txl.lib().txl_last_error()
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(txl, "_lib", None)
     monkeypatch.setattr(txl, "_LIB_PATH", str(tmp_path / "missing.so"))

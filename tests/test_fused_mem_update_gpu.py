@@ -1,0 +1,101 @@
+"""The combined call txl_relattn_fwd_mem_update (through the C ABI): its
+attention outputs are bit-identical to txl_relattn_fwd's on the same inputs,
+and its new memory is bit-identical to the oracle's Tail_M.  The cases cover
+rows shorter than the 1 KB copy unit and rows with a short last unit, grids
+whose waves finish the copy after the key loop, the masked kernel (window,
+valid memory), the paths that launch the copy kernel after the attention
+(fp32, the short-segment streaming kernel), an empty new memory and the
+benchmark shape."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_xl_relative_rel_amd as txl
+from transformer_xl_relative_rel_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+def _host_bits(t):
+    """CPU tensor as the numpy array the oracle takes (bf16 as uint16 patterns)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# B, H, L, M (attention); d_model, M_cur, mem_len, ext_len (memory); dtype; extra attention arguments
+CASES = [
+    (2, 8, 96, 64, 256, 64, 100, 0, "bf16", {}),          # 512-byte rows; rows from mem and h
+    (2, 8, 96, 64, 520, 200, 150, 0, "bf16", {}),         # 1040-byte rows: second unit 16 bytes
+    (1, 8, 32, 0, 1024, 0, 64, 0, "bf16", {}),            # few workgroups, no memory: copy after the loop
+    (3, 8, 80, 48, 512, 30, 40, 8, "bf16", {}),           # ext_len > 0
+    (2, 8, 96, 64, 256, 64, 0, 0, "bf16", {}),            # mem_len 0: empty new memory
+    (2, 8, 96, 64, 512, 64, 100, 0, "bf16", {"window": 50}),                       # masked kernel
+    (2, 8, 96, 64, 512, 64, 100, 0, "bf16", {"mem_valid": [10, 64]}),             # masked kernel
+    (2, 4, 40, 24, 64, 24, 30, 0, "f32", {}),             # generic kernel, copy kernel after it
+    (1, 16, 128, 1600, 1024, 1600, 1600, 0, "bf16", {}),  # streaming kernel, copy kernel after it
+    (8, 16, 512, 512, 1024, 512, 512, 0, "bf16", {}),     # the benchmark step
+]
+
+
+@pytest.mark.parametrize("B,H,L,M,dm,M_cur,mem_len,ext,dtype,kw", CASES)
+def test_fused_matches_separate_calls_and_oracle(B, H, L, M, dm, M_cur, mem_len, ext, dtype, kw):
+    log(f"case: fused fwd+mem_update B{B} H{H} L{L} M{M} d{dm} M_cur{M_cur} mem_len{mem_len} ext{ext} {dtype} {kw}")
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = synth.relattn_inputs(B, H, L, M, 64, dtype=dtype)
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV).to(dt)
+    q, k, v, r = (t(d[x], td) for x in ("q", "k", "v", "r"))
+    u, vb = t(d["u"], torch.float32), t(d["vb"], torch.float32)
+    kw = dict(kw)
+    if "mem_valid" in kw:
+        kw["mem_valid"] = torch.tensor(kw["mem_valid"], dtype=torch.int32, device=DEV)
+    g = torch.Generator().manual_seed(B * 1000 + dm + M_cur)
+    mem_c = torch.randn((B, M_cur, dm), generator=g).to(td) if M_cur else None
+    h_c = torch.randn((B, L, dm), generator=g).to(td)
+    mem = mem_c.to(DEV) if mem_c is not None else None
+    h = h_c.to(DEV)
+    for rep in range(2):   # a second call on the same buffers: no state carried between launches
+        out, lse, new_mem = txl.relattn_fwd_mem_update(q, k, v, r, u, vb, mem, h, mem_len, ext, want_lse=True, **kw)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = txl.relattn_fwd(q, k, v, r, u, vb, want_lse=True, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), "attention output differs from txl_relattn_fwd"
+        assert torch.equal(lse, ref_lse), "lse differs from txl_relattn_fwd"
+        want = oracle.mem_update(_host_bits(mem_c) if mem_c is not None else None, _host_bits(h_c), mem_len,
+                                 ext_len=ext)
+        assert tuple(new_mem.shape) == want.shape
+        np.testing.assert_array_equal(_bits(new_mem), want.view(np.uint8).reshape(_bits(new_mem).shape))
+
+
+def test_fused_strided_new_memory_leaves_gaps_alone():
+    """new_mem as a view with a batch stride larger than a batch row: the bytes
+    between batch rows are not written."""
+    log("case: fused fwd+mem_update strided new_mem")
+    B, H, L, M, dm, mem_len = 2, 8, 64, 64, 512, 96
+    d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV).to(dt)
+    q, k, v, r = (t(d[x], torch.bfloat16) for x in ("q", "k", "v", "r"))
+    u, vb = t(d["u"], torch.float32), t(d["vb"], torch.float32)
+    g = torch.Generator().manual_seed(7)
+    mem_c = torch.randn((B, M, dm), generator=g).to(torch.bfloat16)
+    h_c = torch.randn((B, L, dm), generator=g).to(torch.bfloat16)
+    big = torch.full((B, mem_len + 5, dm), 3.0, dtype=torch.bfloat16, device=DEV)
+    view = big[:, :mem_len]
+    out, new_mem = txl.relattn_fwd_mem_update(q, k, v, r, u, vb, mem_c.to(DEV), h_c.to(DEV), mem_len, new_mem=view)
+    torch.cuda.synchronize()
+    want = oracle.mem_update(_host_bits(mem_c), _host_bits(h_c), mem_len)
+    np.testing.assert_array_equal(_bits(view), want.view(np.uint8).reshape(_bits(view).shape))
+    assert bool((big[:, mem_len:] == 3.0).all())

@@ -11,7 +11,7 @@ import ctypes
 import os
 
 __all__ = [
-    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_workspace_size", "relattn_bwd",
+    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_fwd_mem_update", "relattn_workspace_size", "relattn_bwd",
     "relattn_bwd_workspace_size", "mem_update", "mem_update_batched", "stack_segment",
     "layer_fwd", "layer_workspace_size", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
@@ -23,7 +23,8 @@ _lib = None
 
 # Every function declared in include/txl.h.
 EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
-            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_bwd_workspace_size", "txl_relattn_bwd",
+            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
+            "txl_relattn_bwd_workspace_size", "txl_relattn_bwd",
             "txl_mem_update", "txl_mem_update_batched",
             "txl_layer_workspace_size", "txl_layer_fwd")
 
@@ -77,6 +78,8 @@ def lib():
     L.txl_relattn_desc_init.argtypes = [dp, i, i, i, i, i, i]
     L.txl_relattn_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     L.txl_relattn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.txl_relattn_fwd_mem_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp, i, vp, i, i, i,
+                                             i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     L.txl_relattn_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     L.txl_relattn_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
     L.txl_mem_update.argtypes = [vp, i, vp, i, vp, i, i, i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
@@ -85,7 +88,7 @@ def lib():
     ldp = ctypes.POINTER(LayerDesc)
     L.txl_layer_workspace_size.argtypes = [ldp, i, ctypes.POINTER(sz)]
     L.txl_layer_fwd.argtypes = [ldp, ctypes.POINTER(LayerWeights), vp, vp, i, vp, vp, vp, vp, sz, vp]
-    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd",
+    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
                  "txl_relattn_bwd_workspace_size", "txl_relattn_bwd", "txl_mem_update",
                  "txl_mem_update_batched", "txl_layer_workspace_size", "txl_layer_fwd"):
         getattr(L, name).restype = i
@@ -159,6 +162,14 @@ def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, ls
     memory rows of batch row b.
     Returns out (and lse [B, H, L] float32 when ``want_lse`` or ``lse`` is given).
     """
+    d, out, lse, workspace, ws_bytes = _fwd_args(q, k, v, r_k, u, vb, scale, out, lse, want_lse, splits, workspace,
+                                                 window, mem_valid)
+    _check(lib().txl_relattn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
+                                 _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def _fwd_args(q, k, v, r_k, u, vb, scale, out, lse, want_lse, splits, workspace, window, mem_valid):
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
@@ -178,9 +189,35 @@ def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, ls
     if need.value and workspace is None:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().txl_relattn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
-                                 _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
-    return (out, lse) if lse is not None else out
+    return d, out, lse, workspace, ws_bytes
+
+
+def relattn_fwd_mem_update(q, k, v, r_k, u, vb, mem, h, mem_len: int, ext_len: int = 0, *, new_mem=None,
+                           scale: float | None = None, out=None, lse=None, want_lse: bool = False, splits: int = 0,
+                           workspace=None, stream=None, window: int = 0, mem_valid=None):
+    """relattn_fwd and mem_update(mem, h, mem_len, ext_len) in one call (txl_relattn_fwd_mem_update).
+
+    Arguments as for those two; returns (out, new_mem) or (out, lse, new_mem).
+    """
+    import torch
+    d, out, lse, workspace, ws_bytes = _fwd_args(q, k, v, r_k, u, vb, scale, out, lse, want_lse, splits, workspace,
+                                                 window, mem_valid)
+    B, L, dm = h.shape
+    M_cur = 0 if mem is None else mem.shape[1]
+    M_new = _new_len(M_cur, L, mem_len, ext_len)
+    if new_mem is None:
+        new_mem = torch.empty((B, M_new, dm), dtype=h.dtype, device=h.device)
+    for t in (mem, h, new_mem):
+        if t is not None and t.numel() and (t.stride(-1) != 1 or t.stride(-2) != dm):
+            raise ValueError("rows must be contiguous")
+    got = ctypes.c_int(-1)
+    _check(lib().txl_relattn_fwd_mem_update(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _ptr(mem if M_cur else None), M_cur, _ptr(h), L, _ptr(new_mem), mem_len, ext_len,
+        B, dm, _dtype_code(h), mem.stride(0) if M_cur else 0, h.stride(0), new_mem.stride(0), ctypes.byref(got),
+        _stream(stream)))
+    assert got.value == M_new
+    return (out, lse, new_mem) if lse is not None else (out, new_mem)
 
 
 def _bwd_desc(q, k, v, r_k, out, dout, scale, window, mem_valid) -> RelAttnDesc:

@@ -11,6 +11,21 @@ namespace txl {
 constexpr int kBK = 64;
 constexpr int kWaves = 4;
 
+// One Tail_M update carried out by an attention launch (nchunks = 0: none).
+// Work unit: 1 KB chunk `ch` of row t of batch row b of the new memory,
+// numbered ((b * M_new + t) * cpr + ch); source row beg + t of [mem; h].
+struct FusedCopy {
+    const unsigned char *mem, *h;   // batch row 0 of each source
+    unsigned char *dst;
+    int64_t mem_bs, h_bs, new_bs;   // batch strides in bytes
+    int M_cur, beg, M_new, B;
+    int row_bytes;                  // bytes per row, a multiple of 16
+    int cpr;                        // 1 KB chunks per row
+    int nchunks;                    // B * M_new * cpr
+    int inc_ch, inc_t, inc_b;       // chunk-number stride between a wave's chunks (the launch's
+                                    // wave count) as (batch row, row, chunk) steps; set at launch
+};
+
 struct RelAttnArgs {
     const void *q, *k, *v, *r;
     const float *u, *vb;
@@ -28,6 +43,7 @@ struct RelAttnArgs {
                       // 2 heads h = x (mod 8) of every batch row on XCD x (H % 8 == 0)
     const int *mem_valid;   // [B] valid memory rows per batch row, or NULL (all M)
     int window;             // > 0: query i sees keys j >= i + M + 1 - window
+    FusedCopy cp;           // memory update done by the bf16 throughput kernel's waves
 };
 
 // First key visible to query i of batch row b: keys below it are masked.

@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "bf16_tiles.h"
@@ -386,6 +388,63 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
     stage_d(IC<1>{});
 }
 
+// ---------------------------------------------------------------------------
+// Memory update (Tail_M) carried by the attention launch.  The copy's 1 KB
+// chunks, numbered ((b M_new + t) cpr + ch) for chunk ch of row t of batch
+// row b of the new memory, are dealt to the launch's waves round-robin: wave
+// w of W takes chunks w, w + W, ...  A wave walks its chunks as scalar
+// coordinates (b, t, ch) advanced by the host's increments with carries, so
+// the key loop needs no division.  A chunk lies in one row, so its source and
+// destination rows are wave-uniform buffer resources and each lane moves 16
+// bytes; lanes past the row end read zeros and their writes are dropped.
+typedef const __attribute__((address_space(4))) FusedCopy KFusedCopy;
+
+// The copy's arguments, read from the kernel argument segment (the launch's
+// only argument is the RelAttnArgs) through a pointer the compiler cannot
+// follow, so that every use reloads them with scalar loads instead of holding
+// them in scalar registers across the key loop.
+__device__ __forceinline__ KFusedCopy *fused_copy_args()
+{
+    KFusedCopy *c = (KFusedCopy *)((const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr() +
+                                   offsetof(RelAttnArgs, cp));
+    asm volatile("" : "+s"(c));
+    return c;
+}
+
+struct CopyPos {
+    int b, t, ch;      // batch row, row of the new memory, 1 KB chunk of the row
+};
+
+__device__ __forceinline__ CopyPos copy_first(KFusedCopy *c, int w)
+{
+    const int cpr = c->cpr, mn = c->M_new;
+    const int row = w / cpr;
+    return CopyPos{row / mn, row % mn, w % cpr};
+}
+
+__device__ __forceinline__ void copy_advance(KFusedCopy *c, CopyPos &p)
+{
+    p.ch += c->inc_ch;
+    const int c1 = p.ch >= c->cpr;
+    p.ch -= c1 ? c->cpr : 0;
+    p.t += c->inc_t + c1;
+    const int c2 = p.t >= c->M_new;
+    p.t -= c2 ? c->M_new : 0;
+    p.b += c->inc_b + c2;
+}
+
+// source and destination rows of chunk p (valid for p.b < B)
+__device__ __forceinline__ void copy_rows(KFusedCopy *c, const CopyPos &p, __amdgpu_buffer_rsrc_t &src,
+                                          __amdgpu_buffer_rsrc_t &dst)
+{
+    const int sr = c->beg + p.t;                  // row of [mem; h]
+    const int rb = c->row_bytes;
+    const unsigned char *s = sr < c->M_cur ? c->mem + p.b * c->mem_bs + (int64_t)sr * rb
+                                           : c->h + p.b * c->h_bs + (int64_t)(sr - c->M_cur) * rb;
+    src = make_rsrc(s, (uint32_t)rb);
+    dst = make_rsrc(c->dst + p.b * c->new_bs + (int64_t)p.t * rb, (uint32_t)rb);
+}
+
 template <bool LOWER>
 __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 {
@@ -393,6 +452,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sr[2][RQ * TILE_CH];
     __shared__ __attribute__((aligned(16))) float sskew[NW][SKEW];
+    __shared__ __attribute__((aligned(16))) u32x4 scopy[NW][64];   // one staged Tail_M chunk per wave
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -539,11 +599,61 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         }
     }
 
+    // Tail_M chunks of this wave: inside the key loop one every cstride tiles
+    // (the copy steps, staggered over the workgroup's waves so that the copy's
+    // traffic is spread over the loop), staged in LDS by a direct load in one
+    // copy step and written out at the start of the next (after the wait and
+    // barrier that end every tile), so the copy holds no vector registers
+    // across the tile body; the rest after the loop.  pos is the staged chunk
+    // while one is staged, else the next to load.
+    CopyPos pos{0x7fffffff, 0, 0};    // past the last batch row: no copy
+    if (fused_copy_args()->nchunks > 0) pos = copy_first(fused_copy_args(), (int)blockIdx.x * NW + wave);
+    bool staged = false;
+    const uint32_t scopy_base = __builtin_amdgcn_readfirstlane(lds_addr(&scopy[wave][0]));
+    auto lane16 = [&]() {
+        uint32_t l = 16u * (uint32_t)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    int cstride = 1, cphase = 0;
+    {
+        KFusedCopy *c = fused_copy_args();
+        if (c->nchunks > 0) {
+            const int waves = (int)gridDim.x * NW;
+            const int cpw = (c->nchunks + waves - 1) / waves;     // chunks per wave
+            cstride = max(1, (kt1 - kt0) / (cpw + 1));
+            cphase = wave % cstride;
+        }
+    }
+    int ccount = cphase;      // tiles until this wave's next copy step
+    auto copy_out = [&]() {
+        if (staged) {
+            KFusedCopy *c = fused_copy_args();
+            __amdgpu_buffer_rsrc_t src, dst;
+            copy_rows(c, pos, src, dst);
+            const uint32_t l16 = lane16();
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(&scopy[wave][0]) + l16);
+            __builtin_amdgcn_raw_buffer_store_b128(val, dst, 1024u * pos.ch + l16, 0, 0);
+            copy_advance(c, pos);
+            staged = false;
+        }
+    };
+
     // one key tile: stage the next tile, compute this one, wait
     auto step = [&](auto ACT, auto MC, int kt) {
         constexpr bool ACTIVE = decltype(ACT)::value != 0;
         constexpr bool MASKED = decltype(MC)::value != 0;
         const int j0 = kt * BK;
+        if (ccount-- == 0) {       // a copy step of this wave
+            ccount = cstride - 1;
+            copy_out();
+            if (pos.b < fused_copy_args()->B) {
+                __amdgpu_buffer_rsrc_t src, dst;
+                copy_rows(fused_copy_args(), pos, src, dst);
+                load_lds16(src, 1024u * pos.ch + lane16(), scopy_base);
+                staged = true;
+            }
+        }
         if (kt + 1 < kt1) {
             load_kv(kt + 1);
             load_r_quarter(kt + RQ - 1);
@@ -581,6 +691,18 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
             else for (; kt < e; ++kt) step(IC<1>{}, IC<0>{}, kt);
         } else {
             for (; kt < e; ++kt) step(IC<0>{}, IC<0>{}, kt);
+        }
+    }
+
+    // the last staged chunk has landed (every tile ends with a full wait)
+    copy_out();
+    if (fused_copy_args()->nchunks > 0) {
+        for (; pos.b < fused_copy_args()->B; copy_advance(fused_copy_args(), pos)) {
+            __amdgpu_buffer_rsrc_t src, dst;
+            copy_rows(fused_copy_args(), pos, src, dst);
+            const uint32_t l16 = lane16();
+            const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(src, 1024u * pos.ch + l16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(val, dst, 1024u * pos.ch + l16, 0, 0);
         }
     }
 
@@ -914,10 +1036,19 @@ hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t 
     return launch_relattn_combine(a, 1, dh, s);
 }
 
-hipError_t launch_relattn_bf16(const RelAttnArgs &a, int dh, hipStream_t s)
+hipError_t launch_relattn_bf16(const RelAttnArgs &args, int dh, hipStream_t s)
 {
     if (dh != DH) return hipErrorInvalidValue;
-    const int blocks = a.nqb * a.B * a.H * a.nsplit;
+    const int blocks = args.nqb * args.B * args.H * args.nsplit;
+    RelAttnArgs a = args;
+    if (a.cp.nchunks > 0) {
+        // a wave's next chunk is the launch's wave count further on
+        const int64_t waves = (int64_t)blocks * NW, cpb = (int64_t)a.cp.M_new * a.cp.cpr;
+        const int64_t rem = waves % cpb;
+        a.cp.inc_b = (int)std::min<int64_t>(waves / cpb, a.cp.B);
+        a.cp.inc_t = (int)(rem / a.cp.cpr);
+        a.cp.inc_ch = (int)(rem % a.cp.cpr);
+    }
     if (a.window > 0 || a.mem_valid)
         hipLaunchKernelGGL(relattn_fwd_bf16_kernel<true>, dim3(blocks), dim3(NTHR), 0, s, a);
     else

@@ -196,9 +196,12 @@ txl_status txl_relattn_workspace_size(const txl_relattn_desc *d, size_t *bytes)
     return ok();
 }
 
-txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void *k, const void *v, const void *r_k,
-                           const float *u, const float *vb, void *out, float *lse, void *workspace,
-                           size_t workspace_bytes, void *stream)
+// Every check of txl_relattn_fwd, then its launch arguments and plan; `ext`
+// receives the byte extents of q, k, v, r_k, out, lse and the workspace
+// (empty where absent) for the fused call's alias checks.
+static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const void *k, const void *v, const void *r_k,
+                              const float *u, const float *vb, void *out, float *lse, void *workspace,
+                              size_t workspace_bytes, txl::RelAttnArgs &a, Plan &p, Extent (&ext)[7])
 {
     txl_status s = check_desc(d);
     if (s != TXL_OK) return s;
@@ -223,8 +226,13 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
         for (const Extent &e : ins)
             if (overlap(el, e)) return fail(TXL_ERR_ALIAS, "lse overlaps an input tensor");
     }
-    const Plan p = plan_relattn(*d);
-    txl::RelAttnArgs a{};
+    for (Extent &e : ext) e = Extent{0, 0};
+    for (int t = 0; t < 4; ++t) ext[t] = ins[t];
+    ext[4] = eo;
+    if (lse) ext[5] = Extent{reinterpret_cast<uintptr_t>(lse),
+                             reinterpret_cast<uintptr_t>(lse) + (size_t)d->B * d->H * d->L * sizeof(float)};
+    p = plan_relattn(*d);
+    a = txl::RelAttnArgs{};
     a.q = q; a.k = k; a.v = v; a.r = r_k; a.u = u; a.vb = vb; a.out = out; a.lse = lse;
     if (p.nsplit > 1) {
         if (!workspace || workspace_bytes < p.ws_bytes)
@@ -237,6 +245,7 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
         a.part_o = static_cast<float *>(workspace);
         a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
         const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + p.ws_bytes};
+        ext[6] = ew;
         if (overlap(ew, eo)) return fail(TXL_ERR_ALIAS, "workspace overlaps out");
         for (const Extent &e : ins)
             if (overlap(ew, e)) return fail(TXL_ERR_ALIAS, "workspace overlaps an input tensor");
@@ -254,9 +263,26 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     a.remap = (d->H % 8 == 0) ? 2 : ((d->B * d->H) % 8 == 0 ? 1 : 0);
     a.mem_valid = d->mem_valid;
     a.window = d->window;
-    hipError_t e = p.stream ? txl::launch_relattn_bf16_stream(a, d->dh, static_cast<hipStream_t>(stream))
-                   : p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
-                            : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
+    return TXL_OK;
+}
+
+static hipError_t fwd_launch(const txl_relattn_desc *d, const Plan &p, const txl::RelAttnArgs &a, void *stream)
+{
+    return p.stream ? txl::launch_relattn_bf16_stream(a, d->dh, static_cast<hipStream_t>(stream))
+           : p.fast ? txl::launch_relattn_bf16(a, d->dh, static_cast<hipStream_t>(stream))
+                    : txl::launch_relattn(a, d->dtype, d->dh, p.rb, static_cast<hipStream_t>(stream));
+}
+
+txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void *k, const void *v, const void *r_k,
+                           const float *u, const float *vb, void *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    txl::RelAttnArgs a;
+    Plan p;
+    Extent ext[7];
+    const txl_status s = fwd_prepare(d, q, k, v, r_k, u, vb, out, lse, workspace, workspace_bytes, a, p, ext);
+    if (s != TXL_OK) return s;
+    const hipError_t e = fwd_launch(d, p, a, stream);
     if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -349,9 +375,10 @@ txl_status txl_relattn_bwd(const txl_relattn_desc *d, const void *q, const void 
     return ok();
 }
 
-static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur, const void *const *h, int L,
-                                    void *const *new_mem, int mem_len, int ext_len, int B, int d, int dtype,
-                                    int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new, void *stream)
+// Every check of txl_mem_update(_batched), then its launch arguments.
+static txl_status mem_update_prepare(int n_buf, const void *const *mem, int M_cur, const void *const *h, int L,
+                                     void *const *new_mem, int mem_len, int ext_len, int B, int d, int dtype,
+                                     int64_t mem_bs, int64_t h_bs, int64_t new_bs, txl::MemUpdateArgs &a)
 {
     if (n_buf < 1 || n_buf > txl::kMaxMemBuffers)
         return fail(TXL_ERR_INVALID_ARG, "n_buf must be in [1, %d] (got %d)", txl::kMaxMemBuffers, n_buf);
@@ -373,7 +400,7 @@ static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur
     if ((B > 1 && M_cur > 0 && mem_bs < (int64_t)M_cur * d) || (B > 1 && L > 0 && h_bs < (int64_t)L * d) ||
         (B > 1 && mnew > 0 && new_bs < (int64_t)mnew * d))
         return fail(TXL_ERR_INVALID_ARG, "batch stride smaller than one batch row");
-    txl::MemUpdateArgs a{};
+    a = txl::MemUpdateArgs{};
     for (int i = 0; i < n_buf; ++i) {
         if (M_cur > 0 && !mem[i]) return fail(TXL_ERR_INVALID_ARG, "mem[%d] is NULL with M_cur=%d", i, M_cur);
         if (L > 0 && !h[i]) return fail(TXL_ERR_INVALID_ARG, "h[%d] is NULL", i);
@@ -409,7 +436,18 @@ static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur
     a.M_cur = M_cur; a.beg = beg; a.M_new = mnew; a.B = B;
     a.row_chunks = (int)(row / 16);
     a.mem_bs = mem_bs * (int64_t)es; a.h_bs = h_bs * (int64_t)es; a.new_bs = new_bs * (int64_t)es;
-    if (M_new) *M_new = mnew;
+    return TXL_OK;
+}
+
+static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur, const void *const *h, int L,
+                                    void *const *new_mem, int mem_len, int ext_len, int B, int d, int dtype,
+                                    int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new, void *stream)
+{
+    txl::MemUpdateArgs a;
+    const txl_status s = mem_update_prepare(n_buf, mem, M_cur, h, L, new_mem, mem_len, ext_len, B, d, dtype, mem_bs,
+                                            h_bs, new_bs, a);
+    if (s != TXL_OK) return s;
+    if (M_new) *M_new = a.M_new;
     hipError_t e = txl::launch_mem_update(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(TXL_ERR_HIP, "mem_update launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -431,6 +469,72 @@ txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, 
         return fail(TXL_ERR_INVALID_ARG, "pointer arrays must not be NULL");
     return mem_update_common(n_buf, mem, M_cur, h, L, new_mem, mem_len, ext_len, B, d, dtype, mem_bs, h_bs, new_bs,
                              M_new, stream);
+}
+
+txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, const void *k, const void *v,
+                                      const void *r_k, const float *u, const float *vb, void *out, float *lse,
+                                      void *workspace, size_t workspace_bytes, const void *mem, int M_cur,
+                                      const void *h, int L_h, void *new_mem, int mem_len, int ext_len, int B_m,
+                                      int d_model, int dtype_m, int64_t mem_bs, int64_t h_bs, int64_t new_bs,
+                                      int *M_new, void *stream)
+{
+    txl::RelAttnArgs a;
+    Plan p;
+    Extent ext[7];
+    txl_status s = fwd_prepare(d, q, k, v, r_k, u, vb, out, lse, workspace, workspace_bytes, a, p, ext);
+    if (s != TXL_OK) return s;
+    txl::MemUpdateArgs m;
+    s = mem_update_prepare(1, &mem, M_cur, &h, L_h, &new_mem, mem_len, ext_len, B_m, d_model, dtype_m, mem_bs, h_bs,
+                           new_bs, m);
+    if (s != TXL_OK) return s;
+    // the two run concurrently: the copy's output must not meet anything the
+    // attention reads or writes, nor its inputs anything the attention writes
+    const size_t es = elem_size(dtype_m);
+    const Extent uvb[2] = {{reinterpret_cast<uintptr_t>(u), reinterpret_cast<uintptr_t>(u) + (size_t)d->H * d->dh * 4},
+                           {reinterpret_cast<uintptr_t>(vb), reinterpret_cast<uintptr_t>(vb) + (size_t)d->H * d->dh * 4}};
+    if (m.M_new > 0) {
+        const int cn[2] = {B_m, m.M_new};
+        const int64_t sn[2] = {new_bs, d_model};
+        const Extent en = extent(new_mem, sn, cn, 2, d_model, es);
+        for (const Extent &e : ext)
+            if (overlap(en, e)) return fail(TXL_ERR_ALIAS, "new_mem overlaps a tensor of the attention call");
+        for (const Extent &e : uvb)
+            if (overlap(en, e)) return fail(TXL_ERR_ALIAS, "new_mem overlaps u or vb");
+    }
+    for (int t = 4; t < 7; ++t) {   // out, lse, workspace
+        if (M_cur > 0) {
+            const int cm[2] = {B_m, M_cur};
+            const int64_t sm[2] = {mem_bs, d_model};
+            if (overlap(ext[t], extent(mem, sm, cm, 2, d_model, es)))
+                return fail(TXL_ERR_ALIAS, "mem overlaps an output or the workspace of the attention call");
+        }
+        if (L_h > 0) {
+            const int ch[2] = {B_m, L_h};
+            const int64_t sh[2] = {h_bs, d_model};
+            if (overlap(ext[t], extent(h, sh, ch, 2, d_model, es)))
+                return fail(TXL_ERR_ALIAS, "h overlaps an output or the workspace of the attention call");
+        }
+    }
+    if (M_new) *M_new = m.M_new;
+    hipError_t e;
+    if (p.fast && !p.stream) {
+        // the throughput kernel's waves carry the copy
+        txl::FusedCopy &c = a.cp;
+        c.mem = m.mem[0]; c.h = m.h[0]; c.dst = m.dst[0];
+        c.mem_bs = m.mem_bs; c.h_bs = m.h_bs; c.new_bs = m.new_bs;
+        c.M_cur = m.M_cur; c.beg = m.beg; c.M_new = m.M_new; c.B = m.B;
+        c.row_bytes = m.row_chunks * 16;
+        c.cpr = (c.row_bytes + 1023) / 1024;
+        const int64_t nch = (int64_t)m.B * m.M_new * c.cpr;
+        if (nch >= ((int64_t)1 << 31)) return fail(TXL_ERR_UNSUPPORTED, "the new memory must hold < 2^31 1 KB chunks");
+        c.nchunks = (int)nch;
+        e = fwd_launch(d, p, a, stream);
+    } else {
+        e = fwd_launch(d, p, a, stream);
+        if (e == hipSuccess) e = txl::launch_mem_update(m, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn + mem_update launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"
