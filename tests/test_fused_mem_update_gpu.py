@@ -3,7 +3,7 @@ attention outputs are bit-identical to txl_relattn_fwd's on the same inputs,
 and its new memory is bit-identical to the oracle's Tail_M.  The cases cover
 rows shorter than the 1 KB copy unit and rows with a short last unit, grids
 whose waves finish the copy after the key loop, the masked kernel (window,
-valid memory), the paths that launch the copy kernel after the attention
+valid memory), forced key splits (a larger grid and the combine), the paths that launch the copy kernel after the attention
 (fp32, the short-segment streaming kernel), an empty new memory and the
 benchmark shape."""
 import sys
@@ -45,6 +45,7 @@ CASES = [
     (2, 8, 96, 64, 256, 64, 0, 0, "bf16", {}),            # mem_len 0: empty new memory
     (2, 8, 96, 64, 512, 64, 100, 0, "bf16", {"window": 50}),                       # masked kernel
     (2, 8, 96, 64, 512, 64, 100, 0, "bf16", {"mem_valid": [10, 64]}),             # masked kernel
+    (2, 8, 96, 64, 512, 64, 100, 0, "bf16", {"splits": 3}),                         # key splits + combine
     (2, 4, 40, 24, 64, 24, 30, 0, "f32", {}),             # generic kernel, copy kernel after it
     (1, 16, 128, 1600, 1024, 1600, 1600, 0, "bf16", {}),  # streaming kernel, copy kernel after it
     (8, 16, 512, 512, 1024, 512, 512, 0, "bf16", {}),     # the benchmark step
