@@ -2,6 +2,8 @@
 // kernels.  Not installed; not part of the C ABI.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +47,10 @@ struct RelAttnArgs {
     int window;             // > 0: query i sees keys j >= i + M + 1 - window
     FusedCopy cp;           // memory update done by the bf16 throughput kernel's waves
 };
+// The bf16 throughput kernel reads `cp` at offsetof(RelAttnArgs, cp) in its
+// kernel argument segment (RelAttnArgs is its only argument).
+static_assert(std::is_standard_layout<RelAttnArgs>::value && std::is_trivially_copyable<RelAttnArgs>::value,
+              "kernel arguments are read by byte offset");
 
 // First key visible to query i of batch row b: keys below it are masked.
 __device__ __forceinline__ int key_lo(const RelAttnArgs &a, int b, int i)

@@ -523,6 +523,7 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, 
         c.mem = m.mem[0]; c.h = m.h[0]; c.dst = m.dst[0];
         c.mem_bs = m.mem_bs; c.h_bs = m.h_bs; c.new_bs = m.new_bs;
         c.M_cur = m.M_cur; c.beg = m.beg; c.M_new = m.M_new; c.B = m.B;
+        if (m.row_chunks > 0x7fffffff / 16) return fail(TXL_ERR_UNSUPPORTED, "a memory row must be < 2 GiB");
         c.row_bytes = m.row_chunks * 16;
         c.cpr = (c.row_bytes + 1023) / 1024;
         const int64_t nch = (int64_t)m.B * m.M_new * c.cpr;
