@@ -190,6 +190,11 @@ txl_status txl_mem_update(const void *mem, int M_cur, const void *h, int L, void
                           int ext_len, int B, int d, int dtype, int64_t mem_bs, int64_t h_bs,
                           int64_t new_bs, int *M_new, void *stream);
 
+/* The length M_new = end - beg of the update above for these sizes, without
+ * launching anything, so that a caller can size new_mem before the call.
+ * Returns TXL_ERR_INVALID_ARG for a negative size or a NULL M_new. */
+txl_status txl_mem_update_len(int M_cur, int L, int mem_len, int ext_len, int *M_new);
+
 /* The same update for n_buf independent buffers in ONE launch (the N+1
  * per-layer memories of a layer stack, [XL] "Segment-Level Recurrence").
  * mem, h and new_mem are HOST arrays of n_buf device pointers; all buffers
@@ -207,8 +212,9 @@ txl_status txl_mem_update_batched(int n_buf, const void *const *mem, int M_cur, 
  * and every check are theirs: desc .. workspace_bytes as txl_relattn_fwd,
  * mem .. M_new as txl_mem_update (B_m batch rows of d_model elements of
  * dtype_m).  Because the two run concurrently, new_mem must not overlap q,
- * k, v, r_k, u, vb, out, lse or the workspace, and mem and h must not
- * overlap out, lse or the workspace (TXL_ERR_ALIAS).  With the bf16
+ * k, v, r_k, u, vb, desc->mem_valid, out, lse or the workspace, and mem and
+ * h must not overlap out, lse or the workspace (TXL_ERR_ALIAS).  *M_new is
+ * written only when the call succeeds.  With the bf16
  * throughput kernel (bf16, dh = 64, not the short-segment streaming case)
  * the attention kernel's own waves do the copy, 1 KB chunks spread over its
  * key loop, so the copy rides on HBM bandwidth the attention leaves unused;
@@ -224,6 +230,21 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *desc, const void *
 /* ------------------------------------------------------------------------ */
 /* Decoder layer (relative attention + post-LayerNorm position-wise FF)     */
 /* ------------------------------------------------------------------------ */
+
+/* Library context of the decoder layer: the rocBLAS handle its projections
+ * run on, bound to the device that is current when the context is created.
+ * Creating one allocates (rocBLAS reserves device memory for its handle), so
+ * callers create it once, outside timed or captured regions, and destroy it
+ * when done; the library keeps no hidden per-thread state.  A context may be
+ * used by one thread at a time (txl_layer_fwd sets its stream per call). */
+typedef struct txl_context_s *txl_context;
+
+/* Creates a context on the current device; *ctx receives it.  TXL_ERR_HIP if
+ * rocBLAS cannot create its handle. */
+txl_status txl_context_create(txl_context *ctx);
+/* Destroys a context made by txl_context_create (NULL is a no-op).  Work
+ * already enqueued with it is not waited for; the caller synchronises first. */
+txl_status txl_context_destroy(txl_context ctx);
 
 /* One RelPartialLearnableDecoderLayer forward with pre_lnorm = False and
  * identity dropout ([SRC] RelPartialLearnableMultiHeadAttn.forward,
@@ -278,9 +299,11 @@ typedef struct {
 /* Workspace bytes of txl_layer_fwd for `desc` and M_cur memory rows. */
 txl_status txl_layer_workspace_size(const txl_layer_desc *desc, int M_cur, size_t *bytes);
 
-txl_status txl_layer_fwd(const txl_layer_desc *desc, const txl_layer_weights *w, const void *h_in,
-                         const void *mem, int M_cur, const float *u, const float *vb, void *h_out,
-                         void *workspace, size_t workspace_bytes, void *stream);
+/* `ctx` (from txl_context_create, on the device of the tensors) supplies the
+ * rocBLAS handle; NULL returns TXL_ERR_INVALID_ARG. */
+txl_status txl_layer_fwd(txl_context ctx, const txl_layer_desc *desc, const txl_layer_weights *w,
+                         const void *h_in, const void *mem, int M_cur, const float *u, const float *vb,
+                         void *h_out, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

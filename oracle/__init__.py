@@ -46,6 +46,39 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+_native = None
+
+
+def _load_native():
+    """The same C source built with -O2 -march=native (no fast-math, no FP
+    contraction) for this host, used only to time the oracle as a CPU
+    baseline.  Built per host into the temporary directory (the code is
+    specific to the CPU it was built on), once per process."""
+    global _native
+    with _lock:
+        if _native is not None:
+            return _native
+        import hashlib
+        import tempfile
+        model = ""
+        try:
+            model = next((l for l in open("/proc/cpuinfo") if l.startswith("model name")), "")
+        except OSError:
+            pass
+        tag = hashlib.sha256((model + open(_SRC).read()).encode()).hexdigest()[:16]
+        path = os.path.join(tempfile.gettempdir(), f"txl_oracle_native_{tag}_{os.getpid()}.so")
+        cmd = ["gcc", "-O2", "-march=native", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-Wall", "-Wextra", "-Wno-unused-parameter", _SRC, "-o", path, "-lm"]
+        subprocess.run(cmd, check=True)
+        lib = ctypes.CDLL(path)
+        lib.txo_relattn_fwd_range.argtypes = [_I, _I, _I, _I, _I, ctypes.c_double, _I,
+                                              _D, _D, _D, _D, _D, _D, _D, _D, _I, _I]
+        lib.txo_relattn_fwd_range.restype = _I
+        os.unlink(path)   # the mapping stays valid
+        _native = lib
+        return lib
+
+
 def _load():
     global _lib
     with _lock:
@@ -135,7 +168,7 @@ def relattn_scores(q, k, r, u, vb, M: int, scale: float | None = None, literal: 
 
 def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = False,
                 threads: int = 1, bh_range: tuple[int, int] | None = None,
-                same_length: int = 0, mem_valid=None):
+                same_length: int = 0, mem_valid=None, native: bool = False):
     """Relative attention over all heads.
 
     q [B, H, L, dh]; k, v [B, H, M+L, dh]; r [H, M+L, dh]; u, vb [H, dh].
@@ -146,7 +179,8 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
     ``same_length`` > 0 applies the same_length mask of [SRC]
     MemTransformerLM._forward with that mem_len; ``mem_valid`` ([B] ints in
     [0, M]) hides the oldest M - mem_valid[b] memory rows of batch row b
-    (per-row memory reset).  Both use the direct score form.
+    (per-row memory reset).  Both use the direct score form.  ``native`` runs
+    the same code built for this host's CPU (-march=native; timing only).
     """
     q, k, v, r, u, vb = map(_f64, (q, k, v, r, u, vb))
     B, H, L, dh = q.shape
@@ -156,11 +190,12 @@ def relattn_fwd(q, k, v, r, u, vb, scale: float | None = None, literal: bool = F
     assert r.shape == (H, K, dh) and u.shape == (H, dh) and vb.shape == (H, dh)
     out = np.zeros((B, H, L, dh), dtype=np.float64)
     lse = np.zeros((B, H, L), dtype=np.float64)
-    lib = _load()
+    variant = same_length > 0 or mem_valid is not None
+    assert not (native and (variant or literal)), "the native build serves the direct, unmasked form"
+    lib = _load_native() if native else _load()
     lo, hi = (0, B * H) if bh_range is None else bh_range
     sc = 0.0 if scale is None else float(scale)
     args = (_p(q), _p(k), _p(v), _p(r), _p(u), _p(vb), _p(out), _p(lse))
-    variant = same_length > 0 or mem_valid is not None
     assert not (variant and literal), "the mask variants use the direct form"
     mv = None
     if mem_valid is not None:

@@ -195,3 +195,52 @@ def test_relattn_bwd_rejects_bad_arguments():
     n = ctypes.c_size_t(0)
     assert lib.txl_relattn_bwd_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == OK and n.value > 0
     assert lib.txl_relattn_bwd_workspace_size(ctypes.byref(_desc(dh=128)), ctypes.byref(n)) == EUNSUP
+
+
+def test_fused_mem_update_writes_no_length_on_failure():
+    """A failing call writes nothing, M_new included, also when the failure is
+    found by the fused path's own checks (a 2 GiB memory row)."""
+    vp = ctypes.c_void_p
+    d = _desc(B=1, H=1, L=160, M=0, dh=64)        # bf16 throughput kernel: the copy rides on it
+    d.splits = 1
+    dm = 1 << 30                                   # one bf16 row of 2 GiB
+    got = ctypes.c_int(-1)
+    s = txl.lib().txl_relattn_fwd_mem_update(
+        ctypes.byref(d), vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), vp(FAKE * 4), vp(FAKE * 5), vp(FAKE * 6),
+        vp(FAKE * 7), vp(0), vp(0), 0, vp(0), 0, vp(FAKE * 9), 1, vp(FAKE * 12), 1, 0, 1, dm, txl.BF16, 0, dm, dm,
+        ctypes.byref(got), vp(0))
+    assert s == EUNSUP
+    assert got.value == -1
+    got.value = -1
+    assert _fwd_mem(_desc(B=1, H=1, L=8, M=0, dh=64), out=FAKE) == EALIAS and got.value == -1
+
+
+def test_fused_mem_update_rejects_new_mem_over_mem_valid():
+    d = _desc(B=2, H=1, L=8, M=0, dh=64)
+    d.mem_valid = FAKE * 10 + 4                      # the kernel reads it while the copy writes new_mem
+    assert _fwd_mem(d) == EALIAS
+    d.mem_valid = FAKE * 7 + 4                       # and the attention's out must not cover it either
+    assert _fwd(d) == EALIAS
+
+
+def test_mem_update_len():
+    lib = txl.lib()
+    n = ctypes.c_int(-1)
+    # end = M_cur + max(0, L - ext_len), beg = max(0, end - mem_len), M_new = end - beg
+    for M_cur, L, mem_len, ext, want in ((0, 8, 8, 0, 8), (8, 8, 8, 0, 8), (3, 4, 16, 0, 7), (5, 10, 4, 3, 4),
+                                         (5, 2, 16, 3, 5), (0, 0, 5, 0, 0), (7, 9, 0, 0, 0)):
+        assert lib.txl_mem_update_len(M_cur, L, mem_len, ext, ctypes.byref(n)) == OK
+        assert n.value == want, (M_cur, L, mem_len, ext)
+    assert lib.txl_mem_update_len(-1, 1, 1, 0, ctypes.byref(n)) == EINVAL
+    assert lib.txl_mem_update_len(1, 1, 1, 0, None) == EINVAL
+
+
+def test_layer_fwd_needs_a_context():
+    vp = ctypes.c_void_p
+    ld = txl.LayerDesc(1, 8, 64, 1, 64, 128, 1e-5, 0, 0, None)
+    lw = txl.LayerWeights(*[FAKE * (i + 1) for i in range(len(txl.LAYER_KEYS))])
+    s = txl.lib().txl_layer_fwd(vp(0), ctypes.byref(ld), ctypes.byref(lw), vp(FAKE * 20), vp(0), 0, vp(FAKE * 21),
+                                vp(FAKE * 22), vp(FAKE * 23), vp(FAKE * 24), ctypes.c_size_t(1 << 40), vp(0))
+    assert s == EINVAL
+    assert b"ctx" in txl.lib().txl_last_error()
+    assert txl.lib().txl_context_destroy(vp(0)) == OK

@@ -16,6 +16,8 @@ import oracle
 import transformer_xl_relative_rel_amd as txl
 from transformer_xl_relative_rel_amd import synth
 
+from tests._common import check_close, sharp_inputs
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
@@ -100,3 +102,27 @@ def test_fused_strided_new_memory_leaves_gaps_alone():
     want = oracle.mem_update(_host_bits(mem_c), _host_bits(h_c), mem_len)
     np.testing.assert_array_equal(_bits(view), want.view(np.uint8).reshape(_bits(view).shape))
     assert bool((big[:, mem_len:] == 3.0).all())
+
+
+@pytest.mark.parametrize("std", [None, 0.5])
+def test_fused_bench_step_against_oracle(std):
+    """The benchmark's step itself (B8 H16 dh64 L512 M512 attention and the
+    Tail_M update of a [8, 512, 1024] bf16 memory, one call) against the
+    oracle directly: every out and lse element within the bf16 tolerance, the
+    new memory bit for bit; at the config's input scale and with sharp
+    inputs (std 0.5, u and vb 0.5)."""
+    log(f"case: fused bench step vs oracle, std {std}")
+    B, H, L, M, dm = 8, 16, 512, 512, 1024
+    d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16") if std is None else sharp_inputs(B, H, L, M, std, 1201)
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV).to(dt)
+    q, k, v, r = (t(d[x], torch.bfloat16) for x in ("q", "k", "v", "r"))
+    u, vb = t(d["u"], torch.float32), t(d["vb"], torch.float32)
+    mem_c = torch.from_numpy(synth.round_bf16(synth.normal((B, M, dm), synth.STREAM["mem"]))).to(torch.bfloat16)
+    h_c = torch.from_numpy(synth.round_bf16(synth.normal((B, L, dm), synth.STREAM["h"]))).to(torch.bfloat16)
+    out, lse, new_mem = txl.relattn_fwd_mem_update(q, k, v, r, u, vb, mem_c.to(DEV), h_c.to(DEV), M, want_lse=True)
+    torch.cuda.synchronize()
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=16)
+    check_close(out.float().cpu().numpy().astype(np.float64), want, "bf16", "out")
+    assert np.abs(lse.cpu().numpy() - wlse).max() <= 2e-2
+    want_mem = oracle.mem_update(_host_bits(mem_c), _host_bits(h_c), M)
+    np.testing.assert_array_equal(_bits(new_mem), want_mem.view(np.uint8).reshape(_bits(new_mem).shape))

@@ -141,21 +141,22 @@ def test_bwd_is_deterministic_full_size():
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), n
 
 
-@pytest.mark.parametrize("B,H,L,M,h", [(8, 16, 512, 512, 5), (8, 16, 512, 256, 11), (1, 16, 128, 1600, 3)])
-def test_bwd_full_size_one_head(B, H, L, M, h):
-    """Benchmark shapes: the whole backward on the device, then every gradient
-    of head h (all batch rows: dq, dk, dv of B heads, and dr, du, dvb of head
-    h, which sum over them) against the oracle run on those heads alone."""
-    log(f"case: bwd full size B{B} H{H} L{L} M{M} head {h}")
-    d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16")
+@pytest.mark.parametrize("B,H,L,M,std", [(8, 16, 512, 512, None), (8, 16, 512, 256, None), (1, 16, 128, 1600, None),
+                                         (8, 16, 512, 512, 0.5)])
+def test_bwd_full_size_every_head(B, H, L, M, std):
+    """Benchmark shapes: the whole backward on the device against the oracle's
+    backward of the whole call, every element of all six gradients (all
+    heads and batch rows), at the configs' input scale and with sharp inputs
+    (std 0.5, u and vb 0.5)."""
+    log(f"case: bwd full size B{B} H{H} L{L} M{M} std {std}")
+    if std is None:
+        d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16")
+    else:
+        d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16", std=std, bias_std=0.5, seed=1301)
     d["dout"] = synth.round_bf16(synth.normal((B, H, L, 64), synth.STREAM["dout"], 1.0).astype(np.float32))
     got = run_gpu(d)
-    sub = {x: d[x][:, h:h + 1] for x in ("q", "k", "v", "dout")}
-    sub.update({x: d[x][h:h + 1] for x in ("r", "u", "vb")})
-    want = oracle.relattn_bwd(sub["q"], sub["k"], sub["v"], sub["r"], sub["u"], sub["vb"], sub["dout"], threads=8)
-    got_h = {"dq": got["dq"][:, h:h + 1], "dk": got["dk"][:, h:h + 1], "dv": got["dv"][:, h:h + 1],
-             "dr": got["dr"][h:h + 1], "du": got["du"][h:h + 1], "dvb": got["dvb"][h:h + 1]}
-    check(got_h, want, f"B{B} H{H} L{L} M{M} h{h}")
+    want = oracle.relattn_bwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], d["dout"], threads=16)
+    check(got, want, f"B{B} H{H} L{L} M{M}")
 
 
 def test_bwd_strided_views_of_fused_qkv():

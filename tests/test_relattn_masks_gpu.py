@@ -18,6 +18,8 @@ import oracle
 import transformer_xl_relative_rel_amd as txl
 from transformer_xl_relative_rel_amd import synth
 
+from tests._common import check_close, sharp_inputs
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
@@ -39,18 +41,6 @@ def run_gpu(d, dtype, window=0, mem_valid=None, splits=0):
     out, lse = txl.relattn_fwd(q, k, v, r, u, vb, want_lse=True, window=window, mem_valid=mv, splits=splits)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
-
-
-def check_close(got, want, dtype, what=""):
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = np.abs(got - want)
-    if dtype == "f32":
-        assert err.max() <= 1e-4, f"{what} max err {err.max():.3e}"
-    else:
-        rms = math.sqrt(float(np.mean(want ** 2)))
-        assert err.max() <= 2e-2, f"{what} max err {err.max():.3e}"
-        assert err.mean() <= 2e-3, f"{what} mean err {err.mean():.3e}"
-        assert err.mean() <= 0.02 * rms, f"{what} mean err {err.mean():.3e} vs rms {rms:.3e}"
 
 
 CASES = [
@@ -102,28 +92,63 @@ def test_first_visible_tile_sets_the_max(dh):
     check_close(got, want, "bf16", "out")
 
 
-def test_headline_shape_sampled_rows_with_masks():
+@pytest.mark.parametrize("std", [None, 0.5])
+def test_headline_shape_with_masks_every_element(std):
     # B=8, H=16, dh=64, L=512, M=512 with same_length (window 512) and a
-    # different valid-memory count per batch row; 64 rows checked one by one.
+    # different valid-memory count per batch row; every element against the
+    # oracle, at the config's input scale and with sharp inputs.
     B, H, L, M, dh, window = 8, 16, 512, 512, 64, 512
     mv = [0, 1, 63, 64, 200, 511, 512, 300]
-    log("case: headline shape with window 512 and per-row memory validity")
-    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
+    log(f"case: headline shape with window 512 and per-row memory validity, std {std}")
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16") if std is None else sharp_inputs(B, H, L, M, std, 901)
     got, glse = run_gpu(d, "bf16", window=window, mem_valid=mv)
-    rng = np.random.default_rng(11)
-    rows = [(0, 0, 0), (B - 1, H - 1, L - 1), (1, 3, 0), (2, 5, 511)]
-    rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(L))) for _ in range(60)]
-    want, wl = [], []
-    for b, h, i in rows:
-        row, l = oracle.relattn_row(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], b, h, i, same_length=window,
-                                    mem_valid=mv[b])
-        want.append(row)
-        wl.append(l)
-    g = np.stack([got[b, h, i] for b, h, i in rows])
-    gl = np.array([glse[b, h, i] for b, h, i in rows])
-    check_close(g, np.stack(want), "bf16", "sampled rows")
-    assert np.abs(gl - np.array(wl)).max() <= 2e-2
-    assert np.all(np.isfinite(got))
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=16,
+                                    same_length=window, mem_valid=mv)
+    check_close(got, want, "bf16", "full tensor")
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+SHARP_MASK_CASES = [
+    # B, H, L, M, std, window, mem_valid, splits
+    (2, 8, 300, 200, 0.7, 0, [0, 117], 1),
+    (2, 8, 300, 200, 0.5, 64, None, 1),
+    (2, 8, 512, 512, 0.5, 300, [40, 512], 1),
+    (1, 8, 512, 256, 1.0, 1, None, 1),
+    (2, 8, 160, 77, 0.6, 100, [77, 5], 0),
+]
+
+
+@pytest.mark.parametrize("B,H,L,M,std,window,mem_valid,splits", SHARP_MASK_CASES)
+def test_mask_variant_sharp_inputs(B, H, L, M, std, window, mem_valid, splits):
+    log(f"case: masked bf16 sharp B{B} H{H} L{L} M{M} std{std} window{window} mem_valid{mem_valid} splits{splits}")
+    d = sharp_inputs(B, H, L, M, std, seed=950 + L + M)
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=16,
+                                    same_length=window, mem_valid=mem_valid)
+    got, glse = run_gpu(d, "bf16", window=window, mem_valid=mem_valid, splits=splits)
+    check_close(got, want, "bf16", "out")
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+@pytest.mark.parametrize("L,M,window,target", [(300, 200, 250, 100), (512, 512, 512, 300), (256, 64, 100, 0),
+                                               (512, 256, 200, 199)])
+def test_distance_probe_with_window(L, M, window, target):
+    """[XL] "Relative Shift Golden Test" through the masked throughput kernel:
+    only the position term is non-zero and r row c scores -64 |distance(c) -
+    target| (distance(c) = K-1-c), so every query attends to the key at
+    distance `target`, j = i + M - target, which the window keeps visible
+    (target < window, target <= M); v[j] = e_(j mod 64) shows which key won."""
+    log(f"case: distance probe with window L{L} M{M} window{window} target{target}")
+    K, dh = M + L, 64
+    r = np.zeros((1, K, dh))
+    r[0, :, 0] = -64.0 * np.abs(np.arange(K - 1, -1, -1) - target)
+    vb = np.zeros((1, dh)); vb[0, 0] = 1.0
+    v = np.zeros((1, 1, K, dh)); v[0, 0, np.arange(K), np.arange(K) % dh] = 1.0
+    d = {"q": np.zeros((1, 1, L, dh)), "k": np.zeros((1, 1, K, dh)), "v": v, "r": r, "u": np.zeros((1, dh)), "vb": vb}
+    got, _ = run_gpu(d, "bf16", window=window, splits=1)
+    for i in range(L):
+        j = i + M - target
+        assert np.argmax(got[0, 0, i]) == j % dh, (i, j)
+        assert got[0, 0, i, j % dh] > 0.99
 
 
 def test_invalid_window_is_rejected():

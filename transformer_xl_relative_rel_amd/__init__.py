@@ -7,13 +7,14 @@ If the library is not built, every call raises; there is no fallback.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
 __all__ = [
     "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_fwd_mem_update", "relattn_workspace_size", "relattn_bwd",
     "relattn_bwd_workspace_size", "mem_update", "mem_update_batched", "stack_segment",
-    "layer_fwd", "layer_workspace_size", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
+    "layer_fwd", "layer_workspace_size", "Context", "context", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
 
 F32, BF16 = 0, 1
@@ -25,8 +26,8 @@ _lib = None
 EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
             "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
             "txl_relattn_bwd_workspace_size", "txl_relattn_bwd",
-            "txl_mem_update", "txl_mem_update_batched",
-            "txl_layer_workspace_size", "txl_layer_fwd")
+            "txl_mem_update", "txl_mem_update_len", "txl_mem_update_batched",
+            "txl_context_create", "txl_context_destroy", "txl_layer_workspace_size", "txl_layer_fwd")
 
 # Weight names of one decoder layer, in the order of txl_layer_weights.
 LAYER_KEYS = ("W_qkv", "W_r", "W_o", "ln1_g", "ln1_b", "W1", "b1", "W2", "b2", "ln2_g", "ln2_b")
@@ -87,10 +88,14 @@ def lib():
                                          i, i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     ldp = ctypes.POINTER(LayerDesc)
     L.txl_layer_workspace_size.argtypes = [ldp, i, ctypes.POINTER(sz)]
-    L.txl_layer_fwd.argtypes = [ldp, ctypes.POINTER(LayerWeights), vp, vp, i, vp, vp, vp, vp, sz, vp]
+    L.txl_layer_fwd.argtypes = [vp, ldp, ctypes.POINTER(LayerWeights), vp, vp, i, vp, vp, vp, vp, sz, vp]
+    L.txl_mem_update_len.argtypes = [i, i, i, i, ctypes.POINTER(i)]
+    L.txl_context_create.argtypes = [ctypes.POINTER(vp)]
+    L.txl_context_destroy.argtypes = [vp]
     for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
-                 "txl_relattn_bwd_workspace_size", "txl_relattn_bwd", "txl_mem_update",
-                 "txl_mem_update_batched", "txl_layer_workspace_size", "txl_layer_fwd"):
+                 "txl_relattn_bwd_workspace_size", "txl_relattn_bwd", "txl_mem_update", "txl_mem_update_len",
+                 "txl_mem_update_batched", "txl_context_create", "txl_context_destroy", "txl_layer_workspace_size",
+                 "txl_layer_fwd"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -286,8 +291,10 @@ def relattn_bwd(q, k, v, r_k, u, vb, out, lse, dout, *, scale: float | None = No
 
 
 def _new_len(M_cur: int, L: int, mem_len: int, ext_len: int) -> int:
-    end = M_cur + max(0, L - ext_len)
-    return end - max(0, end - mem_len)
+    """Rows of the new memory, as the library computes them (txl_mem_update_len)."""
+    n = ctypes.c_int(-1)
+    _check(lib().txl_mem_update_len(M_cur, L, mem_len, ext_len, ctypes.byref(n)))
+    return n.value
 
 
 def mem_update(mem, h, mem_len: int, ext_len: int = 0, out=None, stream=None):
@@ -329,6 +336,54 @@ def mem_update_batched(mems, hs, mem_len: int, ext_len: int = 0, outs=None, stre
     return outs
 
 
+class Context:
+    """A library context (txl_context_create) on the device current at
+    creation; txl_layer_fwd needs one.  close() synchronises the device and
+    destroys it; the binding's own contexts (context()) are closed at exit."""
+
+    def __init__(self):
+        h = ctypes.c_void_p(0)
+        _check(lib().txl_context_create(ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            import torch
+            torch.cuda.synchronize()
+            lib().txl_context_destroy(self._h)
+        self._h = None
+
+
+
+_contexts: dict = {}
+
+
+def _close_contexts():
+    for c in _contexts.values():
+        try:
+            c.close()
+        except Exception:
+            pass
+    _contexts.clear()
+
+
+atexit.register(_close_contexts)
+
+
+def context(device=None) -> Context:
+    """The binding's context for `device` (default: the current device), created on first use."""
+    import torch
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    if idx not in _contexts:
+        with torch.cuda.device(idx):
+            _contexts[idx] = Context()
+    return _contexts[idx]
+
+
 def _layer_desc(h_in, w, n_head: int, d_head: int, eps: float) -> LayerDesc:
     B, L, d = h_in.shape
     return LayerDesc(B, L, d, n_head, d_head, w["W1"].shape[0], eps, 0, 0, None)
@@ -343,16 +398,19 @@ def layer_workspace_size(h_in, w, n_head: int, d_head: int, M_cur: int, eps: flo
 
 
 def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, *, eps: float = 1e-5, out=None, workspace=None,
-              stream=None, clamp_len: int = 0, same_length: int = 0, mem_valid=None):
+              stream=None, clamp_len: int = 0, same_length: int = 0, mem_valid=None, ctx: Context | None = None):
     """One post-LN decoder layer (txl_layer_fwd).
 
     h_in [B, L, d] bf16; mem [B, M_cur, d] bf16 or None; w maps LAYER_KEYS to
     tensors (matrices bf16 in nn.Linear [out, in] layout, vectors float32, b1 /
     b2 may be None); u, vb [H, dh] float32.  clamp_len / same_length as in
     [SRC] MemTransformerLM (0 = off); mem_valid: int32 [B] on the device.
+    ctx: a Context on h_in's device (default: the binding's own, context()).
     Returns h_out [B, L, d] bf16.
     """
     import torch
+    if ctx is None:
+        ctx = context(h_in.device)
     M_cur = 0 if mem is None else mem.shape[1]
     desc = _layer_desc(h_in, w, n_head, d_head, eps)
     desc.clamp_len = int(clamp_len)
@@ -372,7 +430,7 @@ def layer_fwd(h_in, mem, w: dict, u, vb, n_head: int, d_head: int, *, eps: float
         workspace = torch.empty(need.value, dtype=torch.uint8, device=h_in.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     lw = LayerWeights(*[(w[k].data_ptr() if w.get(k) is not None else None) for k in LAYER_KEYS])
-    _check(lib().txl_layer_fwd(ctypes.byref(desc), ctypes.byref(lw), _ptr(h_in), _ptr(mem if M_cur else None), M_cur,
+    _check(lib().txl_layer_fwd(ctx.handle, ctypes.byref(desc), ctypes.byref(lw), _ptr(h_in), _ptr(mem if M_cur else None), M_cur,
                                _ptr(u), _ptr(vb), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 

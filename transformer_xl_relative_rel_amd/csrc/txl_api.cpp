@@ -54,6 +54,15 @@ Extent extent(const void *p, const int64_t *stride, const int *count, int ndim, 
 
 bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Rows kept by the memory update ([SRC] MemTransformerLM._update_mems):
+// end = M_cur + max(0, L - ext_len), beg = max(0, end - mem_len), M_new = end - beg.
+int tail_len(int M_cur, int L, int mem_len, int ext_len)
+{
+    const int end = M_cur + (L - ext_len > 0 ? L - ext_len : 0);
+    const int beg = end - mem_len > 0 ? end - mem_len : 0;
+    return end - beg;
+}
+
 // Kernel choice and key-range split of the attention call.
 struct Plan {
     int fast;    // 1: bf16 throughput kernel, 0: generic kernel
@@ -197,11 +206,12 @@ txl_status txl_relattn_workspace_size(const txl_relattn_desc *d, size_t *bytes)
 }
 
 // Every check of txl_relattn_fwd, then its launch arguments and plan; `ext`
-// receives the byte extents of q, k, v, r_k, out, lse and the workspace
-// (empty where absent) for the fused call's alias checks.
+// receives the byte extents of q, k, v, r_k, mem_valid (inputs, 0-4), out,
+// lse and the workspace (outputs, 5-7), empty where absent, for the fused
+// call's alias checks.
 static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const void *k, const void *v, const void *r_k,
                               const float *u, const float *vb, void *out, float *lse, void *workspace,
-                              size_t workspace_bytes, txl::RelAttnArgs &a, Plan &p, Extent (&ext)[7])
+                              size_t workspace_bytes, txl::RelAttnArgs &a, Plan &p, Extent (&ext)[8])
 {
     txl_status s = check_desc(d);
     if (s != TXL_OK) return s;
@@ -215,8 +225,11 @@ static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const vo
     const int K = d->M + d->L;
     const int cq[3] = {d->B, d->H, d->L}, ck[3] = {d->B, d->H, K}, cr[2] = {d->H, K};
     const Extent eo = extent(out, d->o_stride, cq, 3, d->dh, es);
-    const Extent ins[4] = {extent(q, d->q_stride, cq, 3, d->dh, es), extent(k, d->k_stride, ck, 3, d->dh, es),
-                           extent(v, d->v_stride, ck, 3, d->dh, es), extent(r_k, d->r_stride, cr, 2, d->dh, es)};
+    const Extent ins[5] = {extent(q, d->q_stride, cq, 3, d->dh, es), extent(k, d->k_stride, ck, 3, d->dh, es),
+                           extent(v, d->v_stride, ck, 3, d->dh, es), extent(r_k, d->r_stride, cr, 2, d->dh, es),
+                           d->mem_valid ? Extent{reinterpret_cast<uintptr_t>(d->mem_valid),
+                                                 reinterpret_cast<uintptr_t>(d->mem_valid + d->B)}
+                                        : Extent{0, 0}};
     for (const Extent &e : ins)
         if (overlap(eo, e)) return fail(TXL_ERR_ALIAS, "out overlaps an input tensor");
     if (lse) {
@@ -227,9 +240,9 @@ static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const vo
             if (overlap(el, e)) return fail(TXL_ERR_ALIAS, "lse overlaps an input tensor");
     }
     for (Extent &e : ext) e = Extent{0, 0};
-    for (int t = 0; t < 4; ++t) ext[t] = ins[t];
-    ext[4] = eo;
-    if (lse) ext[5] = Extent{reinterpret_cast<uintptr_t>(lse),
+    for (int t = 0; t < 5; ++t) ext[t] = ins[t];
+    ext[5] = eo;
+    if (lse) ext[6] = Extent{reinterpret_cast<uintptr_t>(lse),
                              reinterpret_cast<uintptr_t>(lse) + (size_t)d->B * d->H * d->L * sizeof(float)};
     p = plan_relattn(*d);
     a = txl::RelAttnArgs{};
@@ -245,7 +258,7 @@ static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const vo
         a.part_o = static_cast<float *>(workspace);
         a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
         const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + p.ws_bytes};
-        ext[6] = ew;
+        ext[7] = ew;
         if (overlap(ew, eo)) return fail(TXL_ERR_ALIAS, "workspace overlaps out");
         for (const Extent &e : ins)
             if (overlap(ew, e)) return fail(TXL_ERR_ALIAS, "workspace overlaps an input tensor");
@@ -279,7 +292,7 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
 {
     txl::RelAttnArgs a;
     Plan p;
-    Extent ext[7];
+    Extent ext[8];
     const txl_status s = fwd_prepare(d, q, k, v, r_k, u, vb, out, lse, workspace, workspace_bytes, a, p, ext);
     if (s != TXL_OK) return s;
     const hipError_t e = fwd_launch(d, p, a, stream);
@@ -388,9 +401,8 @@ static txl_status mem_update_prepare(int n_buf, const void *const *mem, int M_cu
     const size_t es = elem_size(dtype);
     const size_t row = (size_t)d * es;
     if (row % 16 != 0) return fail(TXL_ERR_INVALID_ARG, "a row of d=%d elements is not a multiple of 16 bytes", d);
-    const int end = M_cur + (L - ext_len > 0 ? L - ext_len : 0);
-    const int beg = end - mem_len > 0 ? end - mem_len : 0;
-    const int mnew = end - beg;
+    const int mnew = tail_len(M_cur, L, mem_len, ext_len);
+    const int beg = M_cur + (L - ext_len > 0 ? L - ext_len : 0) - mnew;
     if ((int64_t)mnew * (int64_t)(row / 16) >= ((int64_t)1 << 31) || (int64_t)n_buf * B > 65535)
         return fail(TXL_ERR_UNSUPPORTED, "one batch row of the new memory must hold < 2^31 16-byte words and "
                     "n_buf * B must be <= 65535");
@@ -453,6 +465,15 @@ static txl_status mem_update_common(int n_buf, const void *const *mem, int M_cur
     return ok();
 }
 
+txl_status txl_mem_update_len(int M_cur, int L, int mem_len, int ext_len, int *M_new)
+{
+    if (M_cur < 0 || L < 0 || mem_len < 0 || ext_len < 0)
+        return fail(TXL_ERR_INVALID_ARG, "need M_cur, L, mem_len, ext_len >= 0");
+    if (!M_new) return fail(TXL_ERR_INVALID_ARG, "M_new is NULL");
+    *M_new = tail_len(M_cur, L, mem_len, ext_len);
+    return ok();
+}
+
 txl_status txl_mem_update(const void *mem, int M_cur, const void *h, int L, void *new_mem, int mem_len, int ext_len,
                           int B, int d, int dtype, int64_t mem_bs, int64_t h_bs, int64_t new_bs, int *M_new,
                           void *stream)
@@ -480,7 +501,7 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, 
 {
     txl::RelAttnArgs a;
     Plan p;
-    Extent ext[7];
+    Extent ext[8];
     txl_status s = fwd_prepare(d, q, k, v, r_k, u, vb, out, lse, workspace, workspace_bytes, a, p, ext);
     if (s != TXL_OK) return s;
     txl::MemUpdateArgs m;
@@ -501,7 +522,7 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, 
         for (const Extent &e : uvb)
             if (overlap(en, e)) return fail(TXL_ERR_ALIAS, "new_mem overlaps u or vb");
     }
-    for (int t = 4; t < 7; ++t) {   // out, lse, workspace
+    for (int t = 5; t < 8; ++t) {   // out, lse, workspace
         if (M_cur > 0) {
             const int cm[2] = {B_m, M_cur};
             const int64_t sm[2] = {mem_bs, d_model};
@@ -515,10 +536,8 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, 
                 return fail(TXL_ERR_ALIAS, "h overlaps an output or the workspace of the attention call");
         }
     }
-    if (M_new) *M_new = m.M_new;
-    hipError_t e;
-    if (p.fast && !p.stream) {
-        // the throughput kernel's waves carry the copy
+    const bool fused = p.fast && !p.stream;   // the throughput kernel's waves carry the copy
+    if (fused) {
         txl::FusedCopy &c = a.cp;
         c.mem = m.mem[0]; c.h = m.h[0]; c.dst = m.dst[0];
         c.mem_bs = m.mem_bs; c.h_bs = m.h_bs; c.new_bs = m.new_bs;
@@ -529,6 +548,11 @@ txl_status txl_relattn_fwd_mem_update(const txl_relattn_desc *d, const void *q, 
         const int64_t nch = (int64_t)m.B * m.M_new * c.cpr;
         if (nch >= ((int64_t)1 << 31)) return fail(TXL_ERR_UNSUPPORTED, "the new memory must hold < 2^31 1 KB chunks");
         c.nchunks = (int)nch;
+    }
+    // every check has passed: nothing below returns before the launches
+    if (M_new) *M_new = m.M_new;
+    hipError_t e;
+    if (fused) {
         e = fwd_launch(d, p, a, stream);
     } else {
         e = fwd_launch(d, p, a, stream);

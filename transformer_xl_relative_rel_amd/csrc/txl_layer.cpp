@@ -16,7 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
+#include <new>
 #include <string>
 
 #include "internal.h"
@@ -37,18 +37,6 @@ txl_status fail(txl_status s, const char *fmt, ...)
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
     return txl::set_error(s, buf);
-}
-
-// One rocBLAS handle per (thread, device); the stream is set per call.
-rocblas_handle blas_handle(int device)
-{
-    thread_local std::map<int, rocblas_handle> handles;
-    auto it = handles.find(device);
-    if (it != handles.end()) return it->second;
-    rocblas_handle h = nullptr;
-    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
-    handles[device] = h;
-    return h;
 }
 
 // Row-major Y[n][m] (+)= X[n][k] W[m][k]^T for `batch` independent problems.
@@ -144,7 +132,38 @@ Range rng(const void *p, size_t bytes)
 
 }  // namespace
 
+// The context of txl_layer_fwd: one rocBLAS handle, made on `device`.
+struct txl_context_s {
+    int device;
+    rocblas_handle blas;
+};
+
 extern "C" {
+
+txl_status txl_context_create(txl_context *ctx)
+{
+    if (!ctx) return fail(TXL_ERR_INVALID_ARG, "ctx is NULL");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(TXL_ERR_HIP, "hipGetDevice failed");
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success) return fail(TXL_ERR_HIP, "rocblas_create_handle failed");
+    txl_context c = new (std::nothrow) txl_context_s{dev, h};
+    if (!c) {
+        rocblas_destroy_handle(h);
+        return fail(TXL_ERR_HIP, "out of host memory");
+    }
+    *ctx = c;
+    return txl::set_error(TXL_OK, "");
+}
+
+txl_status txl_context_destroy(txl_context ctx)
+{
+    if (!ctx) return txl::set_error(TXL_OK, "");
+    const rocblas_status bs = rocblas_destroy_handle(ctx->blas);
+    delete ctx;
+    if (bs != rocblas_status_success) return fail(TXL_ERR_HIP, "rocblas_destroy_handle failed");
+    return txl::set_error(TXL_OK, "");
+}
 
 txl_status txl_layer_workspace_size(const txl_layer_desc *d, int M_cur, size_t *bytes)
 {
@@ -159,10 +178,11 @@ txl_status txl_layer_workspace_size(const txl_layer_desc *d, int M_cur, size_t *
     return txl::set_error(TXL_OK, "");
 }
 
-txl_status txl_layer_fwd(const txl_layer_desc *d, const txl_layer_weights *w, const void *h_in, const void *mem,
-                         int M_cur, const float *u, const float *vb, void *h_out, void *workspace,
+txl_status txl_layer_fwd(txl_context ctx, const txl_layer_desc *d, const txl_layer_weights *w, const void *h_in,
+                         const void *mem, int M_cur, const float *u, const float *vb, void *h_out, void *workspace,
                          size_t workspace_bytes, void *stream)
 {
+    if (!ctx) return fail(TXL_ERR_INVALID_ARG, "ctx is NULL (create one with txl_context_create)");
     txl_status s = check_layer(d, M_cur);
     if (s != TXL_OK) return s;
     if (!w || !w->W_qkv || !w->W_r || !w->W_o || !w->ln1_g || !w->ln1_b || !w->W1 || !w->W2 || !w->ln2_g ||
@@ -206,8 +226,9 @@ txl_status txl_layer_fwd(const txl_layer_desc *d, const txl_layer_weights *w, co
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(TXL_ERR_HIP, "hipGetDevice failed");
-    rocblas_handle bh = blas_handle(dev);
-    if (!bh) return fail(TXL_ERR_HIP, "rocblas_create_handle failed");
+    if (dev != ctx->device)
+        return fail(TXL_ERR_INVALID_ARG, "ctx was created on device %d, the current device is %d", ctx->device, dev);
+    rocblas_handle bh = ctx->blas;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (rocblas_set_stream(bh, st) != rocblas_status_success) return fail(TXL_ERR_HIP, "rocblas_set_stream failed");
 
