@@ -127,6 +127,23 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *desc, const void *q, const vo
                            const void *r_k, const float *u, const float *vb, void *out, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* txl_relattn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results (bitwise), with no workspace
+ * argument.  When the plan splits the key range, the partial outputs go to
+ * the library's static device scratch of 32 MiB (TXL_NOALLOC_SCRATCH_BYTES),
+ * one per device, held until the process ends; its address is looked up on
+ * the first call on each device.  This entry point calls no hipMalloc,
+ * hipFree or allocating library routine.  A call whose split workspace
+ * (txl_relattn_workspace_size) exceeds the scratch returns TXL_ERR_WORKSPACE
+ * and launches nothing.  All calls on one device share that scratch: calls
+ * that may overlap in time on one device (different streams, or threads
+ * without ordering) race and must be serialised by the caller. */
+#define TXL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+txl_status txl_relattn_fwd_noalloc(const txl_relattn_desc *desc, const void *q, const void *k, const void *v,
+                                   const void *r_k, const float *u, const float *vb, void *out, float *lse,
+                                   void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Relative attention backward                                              */
 /* ------------------------------------------------------------------------ */

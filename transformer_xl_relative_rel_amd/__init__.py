@@ -12,7 +12,7 @@ import ctypes
 import os
 
 __all__ = [
-    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_fwd_mem_update", "relattn_workspace_size", "relattn_bwd",
+    "TxlError", "lib", "lib_path", "relattn_fwd", "relattn_fwd_noalloc", "relattn_fwd_mem_update", "relattn_workspace_size", "relattn_bwd",
     "relattn_bwd_workspace_size", "mem_update", "mem_update_batched", "stack_segment",
     "layer_fwd", "layer_workspace_size", "Context", "context", "LAYER_KEYS", "F32", "BF16", "EXPORTED",
 ]
@@ -24,7 +24,7 @@ _lib = None
 
 # Every function declared in include/txl.h.
 EXPORTED = ("txl_version", "txl_status_string", "txl_last_error", "txl_relattn_desc_init",
-            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
+            "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_noalloc", "txl_relattn_fwd_mem_update",
             "txl_relattn_bwd_workspace_size", "txl_relattn_bwd",
             "txl_mem_update", "txl_mem_update_len", "txl_mem_update_batched",
             "txl_context_create", "txl_context_destroy", "txl_layer_workspace_size", "txl_layer_fwd")
@@ -79,6 +79,7 @@ def lib():
     L.txl_relattn_desc_init.argtypes = [dp, i, i, i, i, i, i]
     L.txl_relattn_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     L.txl_relattn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.txl_relattn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.txl_relattn_fwd_mem_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp, i, vp, i, i, i,
                                              i, i, i64, i64, i64, ctypes.POINTER(i), vp]
     L.txl_relattn_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
@@ -92,7 +93,8 @@ def lib():
     L.txl_mem_update_len.argtypes = [i, i, i, i, ctypes.POINTER(i)]
     L.txl_context_create.argtypes = [ctypes.POINTER(vp)]
     L.txl_context_destroy.argtypes = [vp]
-    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_mem_update",
+    for name in ("txl_relattn_desc_init", "txl_relattn_workspace_size", "txl_relattn_fwd", "txl_relattn_fwd_noalloc",
+                 "txl_relattn_fwd_mem_update",
                  "txl_relattn_bwd_workspace_size", "txl_relattn_bwd", "txl_mem_update", "txl_mem_update_len",
                  "txl_mem_update_batched", "txl_context_create", "txl_context_destroy", "txl_layer_workspace_size",
                  "txl_layer_fwd"):
@@ -171,6 +173,26 @@ def relattn_fwd(q, k, v, r_k, u, vb, *, scale: float | None = None, out=None, ls
                                                  window, mem_valid)
     _check(lib().txl_relattn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb), _ptr(out),
                                  _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def relattn_fwd_noalloc(q, k, v, r_k, u, vb, out, lse=None, *, scale: float | None = None, splits: int = 0,
+                        stream=None, window: int = 0, mem_valid=None):
+    """relattn_fwd through txl_relattn_fwd_noalloc: no device allocation in the
+    library or here (out, and lse if wanted, are the caller's); a key-split
+    workspace comes from the library's static scratch."""
+    import torch
+    for t in (u, vb) + ((lse,) if lse is not None else ()):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("u, vb and lse must be contiguous float32")
+    d = _desc(q, k, r_k, out, v, scale, splits)
+    d.window = int(window)
+    if mem_valid is not None:
+        if mem_valid.dtype != torch.int32 or not mem_valid.is_contiguous() or mem_valid.numel() != q.shape[0]:
+            raise ValueError("mem_valid must be a contiguous int32 tensor of B entries")
+        d.mem_valid = mem_valid.data_ptr()
+    _check(lib().txl_relattn_fwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(r_k), _ptr(u), _ptr(vb),
+                                         _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -126,6 +126,12 @@ size_t relattn_bwd_workspace_bytes(int B, int H, int L, int M);
 void relattn_bwd_carve(RelAttnBwdArgs &a, void *ws);
 hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s);
 
+// Static scratch of the entry points that allocate nothing (noalloc_scratch.hip):
+// its size, and its device address on the current device (taken on the
+// first call there).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_buffer(void **ptr, size_t *bytes);
+
 constexpr int kMaxMemBuffers = 64;
 
 struct MemUpdateArgs {

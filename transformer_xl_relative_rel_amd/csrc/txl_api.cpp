@@ -300,6 +300,34 @@ txl_status txl_relattn_fwd(const txl_relattn_desc *d, const void *q, const void 
     return ok();
 }
 
+txl_status txl_relattn_fwd_noalloc(const txl_relattn_desc *d, const void *q, const void *k, const void *v,
+                                   const void *r_k, const float *u, const float *vb, void *out, float *lse,
+                                   void *stream)
+{
+    // the split workspace, if the plan needs one, is the library's static scratch
+    size_t need = 0;
+    txl_status s = txl_relattn_workspace_size(d, &need);
+    if (s != TXL_OK) return s;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        if (need > txl::kScratchBytes)
+            return fail(TXL_ERR_WORKSPACE,
+                        "this call needs %zu bytes of key-split workspace; the static scratch holds %zu "
+                        "(use txl_relattn_fwd with a workspace, or fewer splits)", need, txl::kScratchBytes);
+        const hipError_t e = txl::scratch_buffer(&ws, &ws_bytes);
+        if (e != hipSuccess) return fail(TXL_ERR_HIP, "static scratch unavailable: %s", hipGetErrorString(e));
+    }
+    txl::RelAttnArgs a;
+    Plan p;
+    Extent ext[8];
+    s = fwd_prepare(d, q, k, v, r_k, u, vb, out, lse, ws, ws_bytes, a, p, ext);
+    if (s != TXL_OK) return s;
+    const hipError_t e = fwd_launch(d, p, a, stream);
+    if (e != hipSuccess) return fail(TXL_ERR_HIP, "relattn launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 // The backward kernels support bf16 with dh = 64 and address one head's rows
 // with 32-bit byte offsets.
 static txl_status check_bwd(const txl_relattn_desc *d)
