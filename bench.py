@@ -100,18 +100,107 @@ def cpu_baseline(d, B, H, L, M, dh, gpu_tflops):
             "context": "pages: 1800+x faster evaluation than a vanilla Transformer, no hardware given"}
 
 
-def recorded_traffic(kernel_src):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
-    kernel source (sha256 match); else None."""
+def recorded_traffic(kernel_src, name="relattn_fwd_bf16_B8H16L512M512"):
+    """HBM bytes per launch of a workload's dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary profiles/<name>_traffic.json, if
+    it was taken on the current kernel source (sha256 match); else None."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "relattn_fwd_bf16_B8H16L512M512_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
+
+
+FWD_SRC = os.path.join(ROOT, "transformer_xl_relative_rel_amd", "csrc", "relattn_fwd_bf16.hip")
+COPY_SRC = os.path.join(ROOT, "transformer_xl_relative_rel_amd", "csrc", "mem_update.hip")
+
+
+def timed_groups(torch, stream, fn, n):
+    """Median over five groups of n back-to-back calls of fn, ms per call (HIP
+    events on the launch stream)."""
+    groups = []
+    for _ in range(5):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for i in range(n):
+            fn(i)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        groups.append(a0.elapsed_time(a1) / n)
+    return sorted(groups)[2]
+
+
+def attention_line(torch, txl, synth, B, H, L, M, name, steps, warmup):
+    """One attention call (txl_relattn_fwd, attention only) at another config
+    of the pages' workloads: algorithmic TFLOP/s and the roofline of its bound
+    (MFMA above the ridge, HBM below it)."""
+    dh = 64
+    dev = "cuda:0"
+    d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    q, k, v, r = (t(d[x], torch.bfloat16) for x in ("q", "k", "v", "r"))
+    u, vb = t(d["u"], torch.float32), t(d["vb"], torch.float32)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    need = txl.relattn_workspace_size(q, k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    fn = lambda i: txl.relattn_fwd(q, k, v, r, u, vb, out=out, workspace=ws if need else None, stream=stream)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ms = timed_groups(torch, stream, fn, steps)
+    F = flops_alg(B, H, L, M, dh)
+    nb = min_bytes(B, H, L, M, dh)
+    tflops = F / (ms * 1e-3) / 1e12
+    gbs = nb / (ms * 1e-3) / 1e9
+    mfma_bound = F / nb > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tflops / PEAK_BF16_TFLOPS, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    roof["traffic"] = recorded_traffic(FWD_SRC, name)
+    roof["kernel_ms"] = round(ms, 5)
+    roof["note"] = "time per call includes every launch of the call (split kernel and combine when the keys are split)"
+    return {"metric": f"rel-attn fwd TFLOP/s at B={B},H={H},dh={dh},L={L},M={M}", "value": round(tflops, 2),
+            "unit": "TFLOP/s", "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic", "algorithmic_bytes": nb, "gb_s": round(gbs, 1),
+            "config": {"workload": f"relattn_fwd B{B} H{H} dh{dh} L{L} M{M} bf16", "B": B, "H": H, "dh": dh, "L": L,
+                       "M": M},
+            "roofline": roof}
+
+
+def mem_update_line(torch, txl, steps, warmup):
+    """The memory update of the 16-layer stack (txl_mem_update_batched): 17
+    buffers of [4, 512, 1024] bf16 memory updated with 512 new rows each
+    (mem_len 512), one launch; HBM-bound copy, GB/s of algorithmic bytes
+    (the new memory read from h and written)."""
+    dev = "cuda:0"
+    nbuf, B, L, M, d = 17, 4, 512, 512, 1024
+    g = torch.Generator(device=dev)
+    g.manual_seed(1111)
+    mems = [torch.randn((B, M, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(nbuf)]
+    hs = [torch.randn((B, L, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(nbuf)]
+    outs = [torch.empty_like(m) for m in mems]
+    stream = torch.cuda.current_stream()
+    fn = lambda i: txl.mem_update_batched(mems, hs, M, outs=outs, stream=stream)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ms = timed_groups(torch, stream, fn, steps)
+    nb = 2 * nbuf * B * M * d * 2
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"metric": "Tail_M memory update GB/s, 17 buffers of [4, 512, 1024] bf16", "value": round(gbs, 1),
+            "unit": "GB/s", "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic", "algorithmic_bytes": nb,
+            "config": {"workload": "mem_update_batched 17 x B4 M512 L512 d1024 bf16", "n_buf": nbuf, "B": B,
+                       "M": M, "L": L, "d": d},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic(COPY_SRC, "mem_update_17x_B4M512d1024"),
+                         "kernel": "mem_update_kernel", "kernel_ms": round(ms, 5)}}
 
 
 def stack_flops(B, L, M, d, H, dh, di):
@@ -177,6 +266,10 @@ def main():
     ap.add_argument("--stack", action="store_true",
                     help="instead of the attention step, time the 16-layer stack workload (B4, d1024, H16, "
                          "d_inner 4096, 8 segments of L512 with mem_len 512) end to end")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the attention step, print one line per other workload: the attention at "
+                         "B8 H16 L512 M256 and at B1 H16 L128 M1600, and the 17-buffer memory update")
+    ap.add_argument("--only", default="", help="with --configs: one of cfg2, cfg4, mem")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one Tail_M copy of this many MiB (bigger than every cache) so that a "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE pass can calibrate its counters against known bytes")
@@ -191,8 +284,24 @@ def main():
     import transformer_xl_relative_rel_amd as txl
     from transformer_xl_relative_rel_amd import synth
 
+    if args.calib_copy_mib > 0:
+        rows = args.calib_copy_mib * 128            # rows of 4096 bf16 = 8 KiB
+        src = torch.empty((1, rows, 4096), dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+        dst = txl.mem_update(None, src, rows)
+        torch.cuda.synchronize()
+        del src, dst
     if args.stack:
         stack_bench(torch, txl)
+        return
+    if args.configs:
+        lines = {"cfg2": lambda: attention_line(torch, txl, synth, 8, 16, 512, 256, "relattn_fwd_bf16_B8H16L512M256",
+                                                args.steps, args.warmup),
+                 "cfg4": lambda: attention_line(torch, txl, synth, 1, 16, 128, 1600,
+                                                "relattn_stream_bf16_B1H16L128M1600", args.steps, args.warmup),
+                 "mem": lambda: mem_update_line(torch, txl, args.steps, args.warmup)}
+        for key, fn in lines.items():
+            if not args.only or args.only == key:
+                print(json.dumps(fn()), flush=True)
         return
 
     dev = "cuda:0"
@@ -221,12 +330,6 @@ def main():
         for _ in range(n):
             step()
 
-    if args.calib_copy_mib > 0:
-        rows = args.calib_copy_mib * 128            # rows of 4096 bf16 = 8 KiB
-        src = torch.empty((1, rows, 4096), dtype=torch.bfloat16, device=dev).fill_(1.0)
-        dst = txl.mem_update(None, src, rows)
-        torch.cuda.synchronize()
-        del src, dst
     run_steps(args.warmup)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

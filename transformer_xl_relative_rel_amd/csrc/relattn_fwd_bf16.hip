@@ -615,17 +615,18 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         asm volatile("" : "+v"(l));
         return l;
     };
-    int cstride = 1, cphase = 0;
+    // tiles until this wave's next copy step; without a copy the countdown
+    // never reaches zero inside the key loop
+    int cstride = 1, ccount = 0x7fffffff;
     {
         KFusedCopy *c = fused_copy_args();
         if (c->nchunks > 0) {
             const int waves = (int)gridDim.x * NW;
             const int cpw = (c->nchunks + waves - 1) / waves;     // chunks per wave
             cstride = max(1, (kt1 - kt0) / (cpw + 1));
-            cphase = wave % cstride;
+            ccount = wave % cstride;
         }
     }
-    int ccount = cphase;      // tiles until this wave's next copy step
     auto copy_out = [&]() {
         if (staged) {
             KFusedCopy *c = fused_copy_args();
@@ -788,10 +789,20 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
     const int g = lane >> 4, n = lane & 15;
     const int nruns = a.nqb;
     const int w = blockIdx.x;
-    const int run = w % nruns;
-    const int rest = w / nruns;
-    const int split = rest % a.nsplit;
-    const int bh = rest / a.nsplit;
+    // XCD-aware order (B*H a multiple of 8): every block of a head runs on one
+    // XCD (workgroup w runs on XCD w % 8), so its K, V and r rows, which all its
+    // runs and key splits read, are fetched into one L2
+    int inh = w, bh;
+    if (a.remap) {
+        const int per = nruns * a.nsplit, j = w >> 3;
+        bh = xcd_pair(a, w & 7, j / per);
+        inh = j % per;
+    } else {
+        bh = w / (nruns * a.nsplit);
+        inh = w - bh * nruns * a.nsplit;
+    }
+    const int run = inh % nruns;
+    const int split = inh / nruns;
     const int b = bh / a.H, h = bh - b * a.H;
     const int BH = a.B * a.H;
     const int L = a.L, M = a.M, K = a.K;
@@ -812,19 +823,6 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
     for (int x = 0; x < NX; ++x) i0[x] = ifirst + 16 * x;
 
     State st;
-    const QBias qb = load_qbias(up, wp, g);
-#pragma unroll
-    for (int x = 0; x < NX; ++x) {
-        const int iq = i0[x] + n;
-        const bool ok = iq < L;
-        const int iqc = ok ? iq : 0;
-        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.mneg[x] = 0.f;
-        st.mref[x] = 0.f;
-    }
 
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
@@ -966,7 +964,22 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
     // tiles with every key visible to the run's first query need no mask
     const int ue = (ifirst + M + 1) / BK;
     StreamFrags fa, fb;
+    // the first tile's loads go out before the query fragments' (they do not
+    // depend on them), so the two memory latencies overlap
     if (kt0 < kt1) issue(kt0, fa);
+    const QBias qb = load_qbias(up, wp, g);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        const bool ok = iq < L;
+        const int iqc = ok ? iq : 0;
+        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.mneg[x] = 0.f;
+        st.mref[x] = 0.f;
+    }
     for (int kt = kt0; kt < kt1; kt += 2) {
         if (kt + 1 < kt1) {
             issue(kt + 1, fb);
