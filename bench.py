@@ -133,10 +133,10 @@ def timed_groups(torch, stream, fn, n):
     return sorted(groups)[2]
 
 
-def attention_line(torch, txl, synth, B, H, L, M, name, steps, warmup):
+def attention_line(torch, txl, synth, B, H, L, M, name, steps, warmup, cpu=True):
     """One attention call (txl_relattn_fwd, attention only) at another config
-    of the pages' workloads: algorithmic TFLOP/s and the roofline of its bound
-    (MFMA above the ridge, HBM below it)."""
+    of the pages' workloads: algorithmic TFLOP/s, the roofline of its bound
+    (MFMA above the ridge, HBM below it) and the oracle timed on the host."""
     dh = 64
     dev = "cuda:0"
     d = synth.relattn_inputs(B, H, L, M, dh, dtype="bf16")
@@ -164,12 +164,15 @@ def attention_line(torch, txl, synth, B, H, L, M, name, steps, warmup):
     roof["traffic"] = recorded_traffic(FWD_SRC, name)
     roof["kernel_ms"] = round(ms, 5)
     roof["note"] = "time per call includes every launch of the call (split kernel and combine when the keys are split)"
-    return {"metric": f"rel-attn fwd TFLOP/s at B={B},H={H},dh={dh},L={L},M={M}", "value": round(tflops, 2),
-            "unit": "TFLOP/s", "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
-            "data": "synthetic", "algorithmic_bytes": nb, "gb_s": round(gbs, 1),
-            "config": {"workload": f"relattn_fwd B{B} H{H} dh{dh} L{L} M{M} bf16", "B": B, "H": H, "dh": dh, "L": L,
-                       "M": M},
-            "roofline": roof}
+    res = {"metric": f"rel-attn fwd TFLOP/s at B={B},H={H},dh={dh},L={L},M={M}", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic", "algorithmic_bytes": nb, "gb_s": round(gbs, 1),
+           "config": {"workload": f"relattn_fwd B{B} H{H} dh{dh} L{L} M{M} bf16", "B": B, "H": H, "dh": dh, "L": L,
+                      "M": M},
+           "roofline": roof}
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline(d, B, H, L, M, dh, tflops)
+    return res
 
 
 def mem_update_line(torch, txl, steps, warmup):
@@ -295,9 +298,10 @@ def main():
         return
     if args.configs:
         lines = {"cfg2": lambda: attention_line(torch, txl, synth, 8, 16, 512, 256, "relattn_fwd_bf16_B8H16L512M256",
-                                                args.steps, args.warmup),
+                                                args.steps, args.warmup, not args.no_cpu),
                  "cfg4": lambda: attention_line(torch, txl, synth, 1, 16, 128, 1600,
-                                                "relattn_stream_bf16_B1H16L128M1600", args.steps, args.warmup),
+                                                "relattn_stream_bf16_B1H16L128M1600", args.steps, args.warmup,
+                                                not args.no_cpu),
                  "mem": lambda: mem_update_line(torch, txl, args.steps, args.warmup)}
         for key, fn in lines.items():
             if not args.only or args.only == key:

@@ -740,76 +740,51 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming path: short segments against a long memory (few query runs, many
-// keys).  One wave per workgroup owns one run of 32 queries and one chunk of
-// key tiles; the chunks of a run are merged by the split combine.  Waves do
-// not share tiles, so K and r fragments come straight from global memory into
-// registers (their lane layout is the MFMA operand layout), one tile ahead in
-// a second register set; only V goes through LDS, for the transposing read.
-// Same arithmetic as the throughput kernel (band MFMA + skew, exp2 domain,
-// deferred rescale, denominator MFMA); no lower key bounds.
+// Streaming path: short segments against a long memory (L <= 128, so at most
+// four 32-query runs per head, and many keys).  One workgroup per (b, h, key
+// split) with one wave per run, one wave per SIMD; the waves share the split's
+// K and V tiles and one ring of r rows in LDS, moved by direct-to-LDS loads
+// of whole 128-byte rows one tile ahead, so the workgroup fetches each byte of
+// its keys once (a wave that loaded its own K and r fragments straight into
+// registers touched 16 rows per 1 KB load and four waves fetched the same
+// tile).  The tile body is the throughput kernel's; the key splits of a head
+// are merged by the split combine.
+constexpr int SNW = 4;   // waves per streaming workgroup at most
 
-// V^T fragments of a 64-key V tile in LDS: vf[ch][dt] is the A operand of the
-// P.V MFMA for keys 32 ch .. 32 ch + 31 and head columns 16 dt .. 16 dt + 15.
-// Lane (g, n) gets V[32 ch + 4 g + e][16 dt + n] (transposing read of rows
-// 4 g .. 4 g + 3) and the rows 16 below.  The row swizzle only depends on
-// bits 1-2 of the row, which 32 ch and +16 leave alone.
-__device__ __forceinline__ void read_vt(bf16x8 (&vf)[NT / 2][NDT], const u32x4 *sv, int g, int n)
+__global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnArgs a)
 {
-    TXL_LDS_AS char *vb = (TXL_LDS_AS char *)(TXL_LDS_AS void *)sv;
-    const int row0 = 4 * g + (n >> 2);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        const int chunk = 2 * dt + ((n >> 1) & 1);
-        const int off = (row0 * CPR + (chunk ^ swz_v(row0))) * 16 + 8 * (n & 1);
-#pragma unroll
-        for (int ch = 0; ch < NT / 2; ++ch) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off + ch * 32 * CPR * 16));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((TXL_LDS_AS i16x4 *)(vb + off + (ch * 32 + 16) * CPR * 16));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            vf[ch][dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-        }
-    }
-}
-
-constexpr int SNV = TILE_CH / 64;   // 16-byte V loads per lane per tile
-
-struct StreamFrags {
-    bf16x8 kf[NT][NKK];    // K fragments of the tile
-    bf16x8 rf[NRB][NKK];   // r fragments of the run's band for the tile
-};
-
-__global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
-{
+    __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
-    __shared__ __attribute__((aligned(16))) float skw[SKEW];
+    __shared__ __attribute__((aligned(16))) u32x4 sr[RQ * TILE_CH];
+    __shared__ __attribute__((aligned(16))) float sskew[SNW][SKEW];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int nruns = a.nqb;
-    const int w = blockIdx.x;
-    // XCD-aware order (B*H a multiple of 8): every block of a head runs on one
-    // XCD (workgroup w runs on XCD w % 8), so its K, V and r rows, which all its
-    // runs and key splits read, are fetched into one L2
-    int inh = w, bh;
-    if (a.remap) {
-        const int per = nruns * a.nsplit, j = w >> 3;
-        bh = xcd_pair(a, w & 7, j / per);
-        inh = j % per;
-    } else {
-        bh = w / (nruns * a.nsplit);
-        inh = w - bh * nruns * a.nsplit;
-    }
-    const int run = inh % nruns;
-    const int split = inh / nruns;
-    const int b = bh / a.H, h = bh - b * a.H;
+    const int nw = a.nqb;   // waves of the workgroup = runs of the head
     const int BH = a.B * a.H;
+    // XCD-aware order: every key split of a head runs on one XCD (workgroup w
+    // runs on XCD w % 8), so the head's K, V and r rows are fetched into one L2
+    const int w = blockIdx.x;
+    int bh, split;
+    if (a.remap) {
+        const int j = w >> 3;
+        bh = xcd_pair(a, w & 7, j / a.nsplit);
+        split = j % a.nsplit;
+    } else {
+        bh = w / a.nsplit;
+        split = w - bh * a.nsplit;
+    }
+    const int b = bh / a.H, h = bh - b * a.H;
     const int L = a.L, M = a.M, K = a.K;
+    const int run = wave;
     const int ifirst = RUNQ * run, ilast = min(ifirst + RUNQ - 1, L - 1);
-    const int ntile = (ilast + M) / BK + 1;
+    const int ntile = (L - 1 + M) / BK + 1;   // tiles up to the last query's bound
     const int kt0 = split * a.tiles_per_split;
     const int kt1 = min(ntile, kt0 + a.tiles_per_split);
+    int i0[NX];
+#pragma unroll
+    for (int x = 0; x < NX; ++x) i0[x] = ifirst + 16 * x;
 
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1];
     const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + b * a.ks[0] + h * a.ks[1];
@@ -817,187 +792,102 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
     const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + h * a.rs[0];
     const float *up = a.u + h * DH;
     const float *wp = a.vb + h * DH;
-    const float c = a.c;
-    int i0[NX];
-#pragma unroll
-    for (int x = 0; x < NX; ++x) i0[x] = ifirst + 16 * x;
 
-    State st;
-
+    // ---- direct loads: wave w moves the 1 KB blocks w, w + nw, ... of each
+    // 8 KB tile (block blk holds rows 8 blk .. 8 blk + 7, lane l row l / 8),
+    // reading the chunk the XOR swizzle puts at that LDS position; the K and r
+    // swizzle of row 8 blk + l / 8 only depends on the parity of blk.  Rows
+    // outside [0, K) read zeros.
+    const int lr = lane >> 3;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
+    const int kch0 = ((lane & (CPR - 1)) ^ swz_k(lr)) * 16, kch1 = ((lane & (CPR - 1)) ^ swz_k(lr + 8)) * 16;
+    const int vch = ((lane & (CPR - 1)) ^ swz_v(lr)) * 16;
     const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
-    // r row of the run's band tile 0 at key tile 0 (below 0 for a ragged last
-    // run: those rows read zeros and only feed discarded query columns)
-    const int rbase0 = L - 1 - (ifirst + RUNQ - 1);
+    const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][0]));
     const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][0]));
-    const int vrow0 = lane / CPR;
-    const int vch = ((lane & (CPR - 1)) ^ swz_v(vrow0)) * 16;   // swz_v is the same for rows 8 apart
-
-    auto issue = [&](int kt, StreamFrags &f) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                f.kf[tt][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                    krs, (uint32_t)((kt * BK + 16 * tt + n) * krow_b + (32 * kk + 8 * g) * 2), 0, 0));
-#pragma unroll
-        for (int u = 0; u < NRB; ++u)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                f.rf[u][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                    rrs, (uint32_t)((rbase0 + kt * BK + 16 * u + n) * rrow_b + (32 * kk + 8 * g) * 2), 0, 0));
+    const uint32_t sr_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0]));
+    // ring quarter q % RQ holds r rows cb + 64 q .. + 63, where cb belongs to
+    // the last (unclamped) query of the workgroup's runs and key 0
+    const int cb = L - RUNQ * nw;
+    auto load_kv = [&](int kt) {
         const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
-#pragma unroll
-        for (int e = 0; e < SNV; ++e)
-            load_lds16(vrs, (uint32_t)((kt * BK + vrow0 + 8 * e) * vrow_b + vch), sv_base + boff + (uint32_t)e * 1024);
+        for (int blk = wave; blk < TILE_CH / 64; blk += nw) {
+            const int row = kt * BK + 8 * blk + lr;
+            const uint32_t loff = boff + (uint32_t)blk * 1024u;
+            load_lds16(krs, (uint32_t)(row * krow_b + ((blk & 1) ? kch1 : kch0)), sk_base + loff);
+            load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + loff);
+        }
     };
-    constexpr int LOADS = NT * NKK + NRB * NKK + SNV;   // vector memory loads per tile
-
-    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-    // one tile from fragments f (K and r in registers, V in sv[kt & 1])
-    auto tile = [&](int kt, const StreamFrags &f, bool masked) {
-        int gg = g, nn = n;
-        asm volatile("" : "+v"(gg), "+v"(nn));
-        const int j0 = kt * BK;
-        f32x4 sc[NX][NT];
-        bf16x8 pf[NX][NT / 2];
-        auto stage_a = [&](auto X) {
-            constexpr int x = decltype(X)::value;
-            const float m = st.mneg[x];
-            f32x4 cin[NBT];
-            if (masked) {
-                const int thi = i0[x] < L ? M + i0[x] - j0 + 15 : -1;
-                const int g4 = 4 * gg;
-#pragma unroll
-                for (int bt = 0; bt < NBT; ++bt)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) cin[bt][v] = (g4 > thi - 16 * bt - v) ? -INFINITY : m;
-            } else {
-                const f32x4 m4 = {m, m, m, m};
-#pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) cin[bt] = m4;
-            }
-            f32x4 acc[NBT];
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(f.rf[bt + 1 - x][0], st.qv[x][0], cin[bt]);
-#pragma unroll
-            for (int kk = 1; kk < NKK; ++kk)
-#pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(f.rf[bt + 1 - x][kk], st.qv[x][kk], acc[bt]);
-            lds_order();
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) lds_store4(skw + skew_row(nn) + 16 * bt + 4 * gg + nn + 1, acc[bt]);
-            lds_order();
-        };
-        auto stage_b = [&](auto X) {
-            constexpr int x = decltype(X)::value;
-            f32x4 cin[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-                cin[tt] = *reinterpret_cast<const f32x4 *>(skw + skew_row(nn) + 16 + 16 * tt + 4 * gg);
-            lds_order();
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x4 acc = cin[tt];
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) acc = mfma(f.kf[tt][kk], st.qu[x][kk], acc);
-                sc[x][tt] = acc;
-            }
-        };
-        auto stage_c = [&](auto X) {
-            constexpr int x = decltype(X)::value;
-            float mx = max3(sc[x][0][0], sc[x][0][1], sc[x][0][2]);
-            mx = max3(mx, sc[x][0][3], sc[x][1][0]);
-            mx = max3(mx, sc[x][1][1], sc[x][1][2]);
-            mx = max3(mx, sc[x][1][3], sc[x][2][0]);
-            mx = max3(mx, sc[x][2][1], sc[x][2][2]);
-            mx = max3(mx, sc[x][2][3], sc[x][3][0]);
-            mx = max3(mx, sc[x][3][1], sc[x][3][2]);
-            mx = fmaxf(mx, sc[x][3][3]);
-            const bool first = kt == kt0;
-            if (first || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
-                const float rmx = row_max4(mx);
-                float dlt;
-                if (first) dlt = (rmx == -INFINITY) ? 0.f : rmx;   // exact max of the chunk's first tile
-                else dlt = fmaxf(rmx, 0.f);                         // only ever raised
-                st.mref[x] += dlt;
-                st.mneg[x] -= dlt;
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) sc[x][tt] -= dlt;
-                const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-dlt);
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] *= alpha;
-                st.lsum[x] *= alpha;
-            }
-#pragma unroll
-            for (int ch = 0; ch < NT / 2; ++ch) {
-                f32x8 p8;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    p8[v] = __builtin_amdgcn_exp2f(sc[x][2 * ch][v]);
-                    p8[4 + v] = __builtin_amdgcn_exp2f(sc[x][2 * ch + 1][v]);
-                }
-                pf[x][ch] = __builtin_convertvector(p8, bf16x8);
-            }
-        };
-        stage_a(IC<0>{});
-        stage_b(IC<0>{});
-        stage_a(IC<1>{});
-        stage_c(IC<0>{});
-        stage_b(IC<1>{});
-        stage_c(IC<1>{});
-        bf16x8 vf[NT / 2][NDT];
-        read_vt(vf, sv[kt & 1], gg, nn);
-#pragma unroll
-        for (int x = 0; x < NX; ++x)
-#pragma unroll
-            for (int ch = 0; ch < NT / 2; ++ch) {
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = mfma(vf[ch][dt], pf[x][ch], st.o[x][dt]);
-                st.lsum[x] = mfma(ones, pf[x][ch], st.lsum[x]);
-            }
+    auto load_r_quarter = [&](int q) {
+        const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
+        for (int blk = wave; blk < TILE_CH / 64; blk += nw) {
+            const int x = 64 * q + 8 * blk + lr;
+            load_lds16(rrs, (uint32_t)((cb + x) * rrow_b + ((blk & 1) ? kch1 : kch0)),
+                       sr_base + qoff + (uint32_t)blk * 1024u);
+        }
     };
-
-    // tiles with every key visible to the run's first query need no mask
-    const int ue = (ifirst + M + 1) / BK;
-    StreamFrags fa, fb;
     // the first tile's loads go out before the query fragments' (they do not
     // depend on them), so the two memory latencies overlap
-    if (kt0 < kt1) issue(kt0, fa);
+    if (kt0 < kt1) {
+        load_kv(kt0);
+#pragma unroll
+        for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
+    }
+
+    State st;
     const QBias qb = load_qbias(up, wp, g);
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
         const int iq = i0[x] + n;
         const bool ok = iq < L;
         const int iqc = ok ? iq : 0;
-        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
+        query_frags(qp + (int64_t)iqc * a.qs[2], ok, a.c, qb, g, st.qu[x], st.qv[x]);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.mneg[x] = 0.f;
         st.mref[x] = 0.f;
     }
-    for (int kt = kt0; kt < kt1; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const LaneOff lo = lane_offsets(g, n);
+    Tile t;
+    t.sr = sr;
+    t.skw = sskew[wave];
+    t.offr = RUNQ * (nw - 1 - run);   // ring row of the run's band tile 0
+    // the run sees keys on tiles [kt0, ke); no key of the run is masked below ue
+    const int ke = min(kt1, (ilast + M) / BK + 1);
+    const int ue = (ifirst + M + 1) / BK;
+    for (int kt = kt0; kt < kt1; ++kt) {
         if (kt + 1 < kt1) {
-            issue(kt + 1, fb);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            load_kv(kt + 1);
+            load_r_quarter(kt + RQ - 1);
         }
-        tile(kt, fa, kt >= ue || ifirst + RUNQ - 1 >= L);
-        if (kt + 1 >= kt1) break;
-        if (kt + 2 < kt1) {
-            issue(kt + 2, fa);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kt < ke) {
+            const int j0 = kt * BK;
+            Blk bk[NX];
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                // band row cc of query n is key j0 + cc + n - 15: visible iff cc <= M + i0 - j0 + 15
+                bk[x].thi = i0[x] < L ? M + i0[x] - j0 + 15 : -1;   // ragged tail: nothing visible
+                bk[x].tlo = -1;
+                bk[x].kmem = 0;
+            }
+            t.sk = sk[kt & 1];
+            t.sv = sv[kt & 1];
+            t.kt = kt;
+            t.first = (kt == kt0);
+            if (kt >= ue) tile_body<false, true>(st, t, bk, g, lo);
+            else tile_body<false, false>(st, t, bk, g, lo);
         }
-        tile(kt + 1, fb, kt + 1 >= ue || ifirst + RUNQ - 1 >= L);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
+        __syncthreads();
     }
 
+    // ---- epilogue: lane (g, n) holds query n, head columns 16 dt + 4 g + v
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
         const int iq = i0[x] + n;
@@ -1013,7 +903,7 @@ __global__ __launch_bounds__(64) void relattn_stream_bf16_kernel(RelAttnArgs a)
             }
             if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
         } else {
-            // an empty chunk (or no visible key in it) leaves o = 0, l = 0 and writes m = -inf
+            // a split in which the query sees no key leaves o = 0, l = 0 and writes m = -inf
             float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[x][dt];
@@ -1041,9 +931,9 @@ int relattn_bf16_stream_runs(int L) { return (L + RUNQ - 1) / RUNQ; }
 
 hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t s)
 {
-    if (dh != DH || a.window > 0 || a.mem_valid) return hipErrorInvalidValue;
-    const int blocks = a.nqb * a.B * a.H * a.nsplit;
-    hipLaunchKernelGGL(relattn_stream_bf16_kernel, dim3(blocks), dim3(64), 0, s, a);
+    if (dh != DH || a.window > 0 || a.mem_valid || a.nqb < 1 || a.nqb > SNW) return hipErrorInvalidValue;
+    const int blocks = a.B * a.H * a.nsplit;   // one workgroup per (b, h, key split), one wave per run
+    hipLaunchKernelGGL(relattn_stream_bf16_kernel, dim3(blocks), dim3(64 * a.nqb), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_relattn_combine(a, 1, dh, s);

@@ -87,19 +87,18 @@ Plan plan_relattn(const txl_relattn_desc &d)
     if (!p.fast && d.dtype == TXL_BF16 && d.dh <= 64 && (int64_t)BH * ceil_div(d.L, 16 * txl::kWaves * 2) >= 256)
         p.rb = 2;
     // Short segments against the memory (few query runs per head, no lower key
-    // bounds) go to the streaming kernel: one wave per (run, key chunk).
+    // bounds) go to the streaming kernel: one workgroup per (b, h, key split), one wave per run.
     p.stream = (p.fast && d.L <= 128 && d.window == 0 && !d.mem_valid) ? 1 : 0;
     p.nqb = p.stream ? txl::relattn_bf16_stream_runs(d.L)
                      : (p.fast ? txl::relattn_bf16_groups_per_head(d.L) : ceil_div(d.L, 16 * txl::kWaves * p.rb));
     const int ntile = ceil_div(d.L + d.M, txl::kBK);   // tiles of the longest query block
     int nsplit = d.splits;
     if (nsplit <= 0) {
-        // the throughput kernel holds one workgroup per CU, the generic one two;
-        // the streaming kernel's one-wave workgroups several per CU
-        const int64_t base = (int64_t)p.nqb * BH;
+        // the throughput and streaming kernels hold one workgroup per CU, the
+        // generic one two; the streaming kernel's workgroups take all runs of a head
+        const int64_t base = p.stream ? (int64_t)BH : (int64_t)p.nqb * BH;
         nsplit = 1;
-        if (p.stream) nsplit = (int)std::min<int64_t>(ntile, (1536 + base - 1) / base);
-        else if (base < 256) nsplit = (int)std::min<int64_t>(ntile, ((p.fast ? 256 : 512) + base - 1) / base);
+        if (base < 256) nsplit = (int)std::min<int64_t>(ntile, ((p.fast ? 256 : 512) + base - 1) / base);
         if (nsplit < 1) nsplit = 1;
     }
     if (nsplit > ntile) nsplit = ntile;
