@@ -1,6 +1,7 @@
 """Parity of the streaming path (short segments against a long memory: bf16,
-dh = 64, L <= 128, no lower key bounds; one wave per query run and key chunk,
-chunks merged by the split combine) with the CPU oracle.  This is the
+dh = 64, L <= 128, no lower key bounds; one workgroup per key split with one
+wave per 32-query run, splits merged by the split combine) with the CPU
+oracle.  This is the
 evaluation regime of the pages: a few new tokens per step attending over a
 long cached memory ([XL] "Segment-Level Recurrence", evaluation with a longer
 memory than in training).
@@ -55,6 +56,21 @@ def test_stream_parity(B, H, L, M, splits):
     want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=8)
     got, glse = run_gpu(d, splits=splits)
     check(got, glse, want, wlse, f"L{L} M{M} splits{splits}")
+
+
+@pytest.mark.parametrize("B,H,L,M,std,splits", [
+    (1, 4, 1, 1600, 0.5, 0), (1, 4, 20, 1600, 0.8, 0), (2, 4, 45, 700, 0.5, 0), (1, 8, 77, 300, 0.7, 2),
+    (1, 4, 100, 64, 0.5, 1), (1, 8, 128, 1600, 0.5, 0), (1, 2, 128, 0, 1.0, 1),
+])
+def test_stream_sharp_inputs(B, H, L, M, std, splits):
+    """Inputs at std 0.5-1.0 (u, vb 0.5), on which a shifted or missing
+    position term falls outside the tolerance: one to four runs per
+    workgroup, ragged last runs, forced and automatic key splits."""
+    log(f"case: stream sharp B{B} H{H} L{L} M{M} std{std} splits{splits}")
+    d = synth.relattn_inputs(B, H, L, M, 64, dtype="bf16", std=std, bias_std=0.5, seed=5100 + L + M)
+    want, wlse = oracle.relattn_fwd(d["q"], d["k"], d["v"], d["r"], d["u"], d["vb"], threads=8)
+    got, glse = run_gpu(d, splits=splits)
+    check(got, glse, want, wlse, f"sharp L{L} M{M} splits{splits}")
 
 
 def test_stream_deterministic():
