@@ -447,11 +447,26 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(RelAttnArgs a)
 {
     using T = typename Elem<BF>::T;
     constexpr int TPR = DH / 4;                     // threads per query row
+    constexpr int RPB = 256 / TPR;                  // query rows per workgroup
     const int BH = a.B * a.H;
-    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    // workgroups per (b, h); with the XCD-aware order the rows of a (b, h) are
+    // combined on the XCD whose L2 holds its partials (workgroup w runs on XCD
+    // w % 8, as in the attention kernels)
+    const int cph = (a.L + RPB - 1) / RPB;
+    const int w = blockIdx.x;
+    int bh, chunk;
+    if (a.remap) {
+        const int j = w >> 3;
+        bh = xcd_pair(a, w & 7, j / cph);
+        chunk = j % cph;
+    } else {
+        bh = w / cph;
+        chunk = w - bh * cph;
+    }
+    const int iq = chunk * RPB + threadIdx.x / TPR;
     const int c4 = (threadIdx.x % TPR) * 4;
-    if (row >= (int64_t)BH * a.L) return;
-    const int bh = (int)(row / a.L), iq = (int)(row - (int64_t)bh * a.L);
+    if (iq >= a.L) return;
+    const int64_t row = (int64_t)bh * a.L + iq;
     const int b = bh / a.H, h = bh - b * a.H;
     const int64_t sstride = (int64_t)BH * a.L;      // rows between consecutive splits
     const int64_t r0 = (int64_t)bh * a.L + iq;
@@ -516,9 +531,8 @@ void launch_combine_dh(const RelAttnArgs &a, dim3 grid, hipStream_t s)
 
 hipError_t launch_relattn_combine(const RelAttnArgs &a, int dtype, int dh, hipStream_t s)
 {
-    const int64_t rows = (int64_t)a.B * a.H * a.L;
     const int rows_per_block = 256 / (dh / 4);
-    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+    const dim3 grid((unsigned)((int64_t)a.B * a.H * ((a.L + rows_per_block - 1) / rows_per_block)));
     if (dtype == 1) {
         if (dh == 32) launch_combine_dh<true, 32>(a, grid, s);
         else if (dh == 64) launch_combine_dh<true, 64>(a, grid, s);
