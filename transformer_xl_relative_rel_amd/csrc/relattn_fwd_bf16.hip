@@ -506,21 +506,6 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     const float *wp = a.vb + h * DH;
     const float c = a.c;              // scale * log2(e)
 
-    State st;
-    // ---- query fragments: c (q + u) and c (q + vb), in fp32, rounded once to bf16
-    const QBias qb = load_qbias(up, wp, g);
-#pragma unroll
-    for (int x = 0; x < NX; ++x) {
-        const int iq = i0[x] + n;
-        const bool ok = run_ok && iq < L;
-        const int iqc = ok ? iq : 0;
-        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.mneg[x] = 0.f;
-        st.mref[x] = 0.f;
-    }
     // per-row memory validity: keys below M - mem_valid[b] are hidden from every query
     int kmem_abs = 0;
     if (LOWER && a.mem_valid) {
@@ -570,6 +555,22 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         load_kv(kt0);
 #pragma unroll
         for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
+    }
+    State st;
+    // ---- query fragments: c (q + u) and c (q + vb), in fp32, rounded once to bf16
+    // (their loads go out after the first tile's, so the two latencies overlap)
+    const QBias qb = load_qbias(up, wp, g);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int iq = i0[x] + n;
+        const bool ok = run_ok && iq < L;
+        const int iqc = ok ? iq : 0;
+        query_frags(qp + (int64_t)iqc * a.qs[2], ok, c, qb, g, st.qu[x], st.qv[x]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st.o[x][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.lsum[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.mneg[x] = 0.f;
+        st.mref[x] = 0.f;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
