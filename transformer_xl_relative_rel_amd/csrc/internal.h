@@ -33,8 +33,12 @@ struct RelAttnArgs {
     const float *u, *vb;
     void *out;
     float *lse;
-    float *part_o;   // [nsplit][B*H][L][dh] unnormalised partial outputs (split path)
+    float *part_o;   // unnormalised partial outputs (split path): [nsplit][B*H][L][dh] row-major, or with
+                     // part_native [nsplit][B*H][ceil(L/16)][dh/16][64] 16-byte groups, group (dt, 16 g + n)
+                     // holding query 16 blk + n, head columns 16 dt + 4 g .. + 3 (the bf16 kernels' MFMA
+                     // result layout, so that a wave stores 1 KB contiguously per instruction)
     float *part_ml;  // [nsplit][B*H][L][2]  running max (log2 units) and denominator
+    int part_native;
     int64_t qs[3], ks[3], vs[3], os[3], rs[2];
     int B, H, L, M, K;
     float c;          // scale * log2(e)

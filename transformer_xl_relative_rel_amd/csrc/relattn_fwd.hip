@@ -481,7 +481,13 @@ __global__ __launch_bounds__(256) void relattn_combine_kernel(RelAttnArgs a)
             const int64_t base = (ok ? s0 + e : 0) * sstride + r0;
             ms[e] = ok ? a.part_ml[base * 2] : -INFINITY;
             ls[e] = ok ? a.part_ml[base * 2 + 1] : 0.f;
-            os[e] = ok ? *reinterpret_cast<const f32x4 *>(a.part_o + base * DH + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            int64_t oi = base * DH + c4;   // row-major
+            if (DH == 64 && a.part_native) {
+                // lane layout of the bf16 kernels: 16-byte group (dt, 16 g + n) of 16-query block iq / 16
+                const int64_t blk = ((ok ? s0 + e : 0) * (int64_t)BH + bh) * ((a.L + 15) >> 4) + (iq >> 4);
+                oi = (blk * (DH / 16 * 64) + (c4 >> 4) * 64 + ((c4 & 15) >> 2) * 16 + (iq & 15)) * 4;
+            }
+            os[e] = ok ? *reinterpret_cast<const f32x4 *>(a.part_o + oi) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         float mnew = mrun;
 #pragma unroll

@@ -728,9 +728,10 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
             }
             if (a.lse && ge == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
         } else {
-            float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
+            // lane layout: group (dt, lane) of the query's 16-query block, 1 KB per store instruction
+            float *po = a.part_o + (((int64_t)split * BH + bh) * ((L + 15) >> 4) + (i0[x] >> 4)) * (NDT * 64 * 4);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * ge) = st.o[x][dt];
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + (64 * dt + 16 * ge + ne) * 4) = st.o[x][dt];
             if (ge == 0) {
                 float *pm = a.part_ml + (((int64_t)split * BH + bh) * L + iq) * 2;
                 pm[0] = (l > 0.f) ? st.mref[x] : -INFINITY;   // no visible key in this split
@@ -904,10 +905,11 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
             }
             if (a.lse && g == 0) a.lse[(int64_t)bh * L + iq] = (st.mref[x] + __log2f(l)) * LN2;
         } else {
-            // a split in which the query sees no key leaves o = 0, l = 0 and writes m = -inf
-            float *po = a.part_o + (((int64_t)split * BH + bh) * L + iq) * DH;
+            // a split in which the query sees no key leaves o = 0, l = 0 and writes m = -inf;
+            // lane layout: group (dt, lane) of the query's 16-query block, 1 KB per store instruction
+            float *po = a.part_o + (((int64_t)split * BH + bh) * ((L + 15) >> 4) + (i0[x] >> 4)) * (NDT * 64 * 4);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g) = st.o[x][dt];
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + (64 * dt + 16 * g + n) * 4) = st.o[x][dt];
             if (g == 0) {
                 float *pm = a.part_ml + (((int64_t)split * BH + bh) * L + iq) * 2;
                 pm[0] = (l > 0.f) ? st.mref[x] : -INFINITY;

@@ -73,6 +73,15 @@ struct Plan {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Bytes of the partial outputs of a split plan (the bf16 kernels store them in
+// their lane layout, padded to whole 16-query blocks), rounded to 256.
+size_t part_o_bytes(const txl_relattn_desc &d, const Plan &p)
+{
+    const int Lp = p.fast ? (d.L + 15) / 16 * 16 : d.L;
+    const size_t bytes = (size_t)p.nsplit * d.B * d.H * Lp * d.dh * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
 Plan plan_relattn(const txl_relattn_desc &d)
 {
     Plan p{};
@@ -104,12 +113,7 @@ Plan plan_relattn(const txl_relattn_desc &d)
     if (nsplit > ntile) nsplit = ntile;
     p.tps = ceil_div(ntile, nsplit);
     p.nsplit = ceil_div(ntile, p.tps);
-    if (p.nsplit > 1) {
-        const size_t rows = (size_t)p.nsplit * BH * d.L;
-        size_t o_bytes = rows * d.dh * sizeof(float);
-        o_bytes = (o_bytes + 255) & ~(size_t)255;
-        p.ws_bytes = o_bytes + rows * 2 * sizeof(float);
-    }
+    if (p.nsplit > 1) p.ws_bytes = part_o_bytes(d, p) + (size_t)p.nsplit * BH * d.L * 2 * sizeof(float);
     return p;
 }
 
@@ -252,10 +256,9 @@ static txl_status fwd_prepare(const txl_relattn_desc *d, const void *q, const vo
                         workspace ? workspace_bytes : (size_t)0);
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
             return fail(TXL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        const size_t rows = (size_t)p.nsplit * d->B * d->H * d->L;
-        size_t o_bytes = (rows * d->dh * sizeof(float) + 255) & ~(size_t)255;
         a.part_o = static_cast<float *>(workspace);
-        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + part_o_bytes(*d, p));
+        a.part_native = p.fast;
         const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + p.ws_bytes};
         ext[7] = ew;
         if (overlap(ew, eo)) return fail(TXL_ERR_ALIAS, "workspace overlaps out");
