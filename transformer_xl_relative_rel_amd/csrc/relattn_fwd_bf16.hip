@@ -40,8 +40,13 @@
 // LDS: double-buffered K and V tiles, two rings of r rows (one per end of the
 // paired query range; a tile needs three 64-row quarters of each, a fourth
 // loads ahead), one skew buffer per wave.  Tiles move HBM -> LDS with
-// direct-to-LDS loads issued one tile ahead; rows are 16-byte chunks with an
-// XOR swizzle so that the 16 lanes of a fragment read hit distinct banks.
+// direct-to-LDS loads issued one tile ahead.  K and r are stored
+// fragment-major: the MFMA operand fragment of 16 rows x 32 columns is one
+// contiguous 1 KB block in lane order, so a fragment read is a linear read of
+// 1 KB (measured ~19 cycles per wave against ~51 for a row-major tile read
+// through a bank-spreading swizzle; the direct loads pick each lane's 16
+// bytes from HBM, so the layout costs nothing).  V keeps row-major rows of
+// 16-byte chunks with an XOR swizzle for the transposing reads.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,15 +62,22 @@ namespace txl {
 namespace {
 
 using namespace tiles;   // vector types, DH = 64, CPR, LN2, mfma, direct-to-LDS loads, buffer resources
-constexpr int NW = 8;            // waves per workgroup (two per SIMD)
-constexpr int RUNQ = 32;         // queries per run (two 16-query blocks)
-constexpr int NX = 2;            // 16-query blocks per wave (one run)
-constexpr int PAIRS = 4;         // run pairs per workgroup (waves w and w + 4 share a SIMD)
 constexpr int BK = 64;           // keys per tile
 constexpr int NT = BK / 16;      // 16-key sub-tiles per tile
 constexpr int NBT = NT + 1;      // band tiles per 16-query block
-constexpr int NRB = NT + 2;      // band tiles per run (two blocks)
 constexpr int RQ = 4;            // ring quarters: three in use plus one loading
+// Work split of a workgroup: XW 16-query blocks per wave (one run of 16 XW
+// queries), 16 / XW waves, runs paired from both ends of a head's query range
+// (waves w and w + NW / 2 take the two runs of a pair and share a SIMD), so a
+// workgroup covers 128 queries at each end whatever XW.
+template <int XW> struct Split {
+    static constexpr int NX = XW;            // 16-query blocks per wave
+    static constexpr int NW = 16 / XW;       // waves per workgroup
+    static constexpr int RUNQ = 16 * XW;     // queries per run
+    static constexpr int PAIRS = NW / 2;     // run pairs per workgroup
+    static constexpr int NRB = NT + XW;      // band tiles per run
+    static constexpr int NTHR = NW * 64;
+};
 // Skew buffer: row n (query n) starts at float 80 n + 4 (n / 4); it is
 // written at columns 1..95 and read at columns 16..79, and consecutive rows
 // start at least 80 floats apart, so no row's writes reach another row's read
@@ -76,19 +88,27 @@ constexpr int RQ = 4;            // ring quarters: three in use plus one loading
 // 16-byte skew loads are aligned.
 __device__ __forceinline__ int skew_row(int n) { return 80 * n + 4 * (n >> 2); }
 constexpr int SKEW = 80 * 15 + 4 * 3 + 96;   // floats per wave
-constexpr int RP = 16 / CPR;     // rows per 256 bytes
 constexpr int NKK = DH / 32;     // MFMA k-steps over dh
 constexpr int NDT = DH / 16;     // 16-wide output tiles over dh
 constexpr int TILE_CH = BK * CPR;              // chunks per K or V tile (and per ring quarter)
-constexpr int NTHR = NW * 64;
-constexpr int LPT = TILE_CH / NTHR;            // 16-byte loads per thread per tile
 constexpr float TAU = 8.0f;      // deferred-rescale threshold (log2 units)
-static_assert(RUNQ * (PAIRS - 1) + 16 * NRB <= 64 * (RQ - 1), "a ring must hold one tile's bands in RQ - 1 quarters");
-static_assert(LPT * NTHR == TILE_CH, "whole tiles per load round");
+static_assert(Split<2>::RUNQ * (Split<2>::PAIRS - 1) + 16 * Split<2>::NRB <= 64 * (RQ - 1) &&
+              Split<1>::RUNQ * (Split<1>::PAIRS - 1) + 16 * Split<1>::NRB <= 64 * (RQ - 1),
+              "a ring must hold one tile's bands in RQ - 1 quarters");
 
-// Swizzle of chunk c in row r: K and r rows (16-row b128 fragment reads), V
-// rows (transposing b64 reads of 4 rows x 32 bytes).
-__device__ __forceinline__ int swz_k(int r) { return ((unsigned)r / RP) & (CPR - 1); }
+// Fragment-major K and r tiles: block (m, kk) of a 64-row tile, 1 KB at byte
+// 1024 (2 m + kk), holds rows 16 m .. 16 m + 15, columns 32 kk .. 32 kk + 31;
+// lane (g, n) of the block (byte 16 (16 g + n)) holds row 16 m + n, columns
+// 32 kk + 8 g .. + 7 -- the A operand layout of a 16x16x32 MFMA.
+constexpr int FRAG = 1024;
+// Byte offset, within its 16-row block's pair of fragments, of the 16-byte
+// chunk that lane l of a direct load fetches when it fills fragment kk: row
+// l % 16 of the block, columns 32 kk + 8 (l / 16) .. + 7.
+__device__ __forceinline__ int frag_src(int l, int kk, int row_bytes)
+{
+    return (l & 15) * row_bytes + 64 * kk + 16 * (l >> 4);
+}
+// Swizzle of chunk c in a V row (transposing b64 reads of 4 rows x 32 bytes).
 __device__ __forceinline__ int swz_v(int r) { return (r & 6) & (CPR - 1); }
 
 __device__ __forceinline__ float row_max4(float x)
@@ -148,8 +168,8 @@ __device__ __forceinline__ void query_frags(const uint16_t *qrow, bool ok, float
     }
 }
 
-// Per-wave state of the two query blocks of the wave's run.
-struct State {
+// Per-wave state of the query blocks of the wave's run.
+template <int NX> struct State {
     bf16x8 qu[NX][NKK], qv[NX][NKK];   // c (q + u), c (q + vb): B operands, lane (g, n) = query n
     f32x4 o[NX][NDT];                   // O^T accumulators (unnormalised)
     f32x4 lsum[NX];                     // softmax denominators (all 4 entries equal)
@@ -168,7 +188,7 @@ struct Blk {
 // whole key loop: the tile, the 32-row half, the sub-tile and the ring slot add
 // wave-uniform amounts (immediate offsets or one scalar base per buffer).
 struct LaneOff {
-    int k0;         // K and r fragments: row n of a 16-row block, chunk g under the swizzle (k-step 1: k0 ^ 64)
+    int k0;         // K and r fragments: 16 * lane (fragment-major blocks)
     int v0;         // V^T: rows 4 g + n / 4 (+ 16 for the upper half, + 32 per chunk) of column block 0
                     // (column block dt: v0 ^ 32 dt)
     int sst, sld;   // skew row: store at column 4 g + n + 1, load at column 16 + 4 g (floats)
@@ -178,7 +198,7 @@ __device__ __forceinline__ LaneOff lane_offsets(int g, int n)
 {
     LaneOff o;
     // chunk (4 kk + g) ^ swz = (g ^ swz) ^ 4 kk: k-step kk flips bit 6 of the byte offset
-    o.k0 = (n * CPR + (g ^ swz_k(n))) * 16;
+    o.k0 = 16 * (16 * g + n);
     // chunk (2 dt + b) ^ swz = 2 (dt ^ swz / 2) + b (swz even): column block dt flips bits 5-6
     const int row0 = 4 * g + (n >> 2);
     o.v0 = (row0 * CPR + (((n >> 1) & 1) ^ swz_v(row0))) * 16 + 8 * (n & 1);
@@ -195,20 +215,19 @@ struct Tile {
     bool first;         // first tile of the key range
 };
 
+// The tile body is split in two halves: H1 (band MFMAs, skew round trip,
+// content MFMAs) reads K and the r ring, H2 (softmax and P.V) reads V, so the
+// throughput kernel can meet its per-tile barrier between them.
+//
 // LOWER: some query has a lower key bound (window or memory validity), so a
 // query's first visible tile need not be the first tile of the range.
 // MASKED: some key of the run is masked on this tile (band rows or key
 // columns); otherwise every band row starts at -m.
-template <bool LOWER, bool MASKED>
-__device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&bk)[NX], int g, const LaneOff &lo)
+template <bool LOWER, bool MASKED, int NX>
+__device__ __forceinline__ void tile_h1(State<NX> &st, const Tile &t, const Blk (&bk)[NX], int g, const LaneOff &lo,
+                                        f32x4 (&sc)[NX][NT])
 {
-    // The derived offsets (k-step 1, column blocks 1-3) are formed per tile
-    // from the two base offsets, made opaque here so that they are not hoisted
-    // out of the key loop as registers of their own.
-    int k0 = lo.k0, v0 = lo.v0;
-    asm volatile("" : "+v"(k0), "+v"(v0));
-    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    const int k0 = lo.k0;
 
     // K fragments (A operands of the content MFMA), shared by the two blocks
     bf16x8 kf[NT][NKK];
@@ -218,23 +237,117 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
-                kf[tt][kk] = *(const TXL_LDS_AS bf16x8 *)(kb + (k0 ^ (64 * kk)) + tt * 16 * CPR * 16);
+                kf[tt][kk] = *(const TXL_LDS_AS bf16x8 *)(kb + k0 + (2 * tt + kk) * FRAG);
     }
     // r fragments of one run: run band tile u holds ring rows offr + 16 u + n.
     // A 16-row band tile never straddles a 64-row quarter (offr is a multiple
     // of 32), so its quarter slot is uniform across the wave.
+    constexpr int NRB = NT + NX;   // band tiles of the run
     bf16x8 rf[NRB][NKK];
-    auto load_r = [&]() {
+    {
         const TXL_LDS_AS char *srb = lds_bytes(t.sr);
         const int offr = t.offr;
 #pragma unroll
         for (int u = 0; u < NRB; ++u) {
             const int x0 = offr + 16 * u;   // wave-uniform
-            const int ubase = (((t.kt + (x0 >> 6)) & (RQ - 1)) * TILE_CH + (x0 & 63) * CPR) * 16;
+            const int ubase = ((t.kt + (x0 >> 6)) & (RQ - 1)) * (TILE_CH * 16) + ((x0 >> 4) & 3) * (2 * FRAG);
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = *(const TXL_LDS_AS bf16x8 *)(srb + ubase + (k0 ^ (64 * kk)));
+            for (int kk = 0; kk < NKK; ++kk) rf[u][kk] = *(const TXL_LDS_AS bf16x8 *)(srb + ubase + k0 + kk * FRAG);
+        }
+    }
+
+    // band MFMA of block x (run band tiles NX-1-x .. NX+3-x: later queries need lower r rows)
+    auto band = [&](auto X, f32x4 (&acc)[NBT]) {
+        constexpr int x = decltype(X)::value;
+        constexpr int h = NX - 1 - x;
+        const bf16x8 *qv = st.qv[x];
+        const float m = st.mneg[x];
+        f32x4 cin[NBT];
+        if constexpr (MASKED) {
+            // band row 16 bt + 4 g + v is visible iff tlo <= row <= thi
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * bt + 4 * g + v;
+                    cin[bt][v] = (row > bk[x].thi || row < bk[x].tlo) ? -INFINITY : m;
+                }
+        } else {
+            const f32x4 m4 = {m, m, m, m};
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) cin[bt] = m4;
+        }
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + h][0], qv[0], cin[bt]);
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk)
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + h][kk], qv[kk], acc[bt]);
+    };
+    // skew of a block's band values into the wave's LDS rows
+    auto skew_store = [&](const f32x4 (&acc)[NBT]) {
+        float *skw = t.skw;
+        lds_order();
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt)   // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
+            lds_store4(skw + lo.sst + 16 * bt, acc[bt]);
+        lds_order();
+    };
+    // read back block x's skewed band values (keys on rows, in key order)
+    auto skew_load = [&](auto X, f32x4 (&cin)[NT]) {
+        constexpr int x = decltype(X)::value;
+        const float *skw = t.skw;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + lo.sld + 16 * tt);
+        lds_order();
+        if (LOWER && MASKED) {
+            // keys below kmem are hidden from every query of the block
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (16 * tt + 4 * g + v < bk[x].kmem) cin[tt][v] = -INFINITY;
         }
     };
+    // content MFMA of block x on top of the skewed band values
+    auto content = [&](auto X, const f32x4 (&cin)[NT]) {
+        constexpr int x = decltype(X)::value;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 acc = cin[tt];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) acc = mfma(kf[tt][kk], st.qu[x][kk], acc);
+            sc[x][tt] = acc;
+        }
+    };
+
+    // Both blocks' band MFMAs first, then the two skew round trips back to
+    // back (one skew buffer per wave: LDS operations of a wave complete in
+    // order, so block 1's stores land after block 0's loads have read), so
+    // that their latencies overlap; then the content MFMAs.
+    f32x4 acc0[NBT], acc1[NBT], cin0[NT], cin1[NT];
+    band(IC<0>{}, acc0);
+    if constexpr (NX > 1) band(IC<1>{}, acc1);
+    skew_store(acc0);
+    skew_load(IC<0>{}, cin0);
+    if constexpr (NX > 1) {
+        skew_store(acc1);
+        skew_load(IC<1>{}, cin1);
+    }
+    content(IC<0>{}, cin0);
+    if constexpr (NX > 1) content(IC<1>{}, cin1);
+}
+
+template <bool LOWER, int NX>
+__device__ __forceinline__ void tile_h2(State<NX> &st, const Tile &t, const LaneOff &lo, f32x4 (&sc)[NX][NT])
+{
+    // column blocks 1-3 of V^T are formed per tile from the base offset
+    int v0 = lo.v0;
+    asm volatile("" : "+v"(v0));
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+
     // V^T fragments (A operands of P.V), read through the transposing LDS read
     bf16x8 vf[NT / 2][NDT];
     auto load_v = [&]() {
@@ -253,71 +366,9 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
             }
     };
 
-    f32x4 sc[NX][NT];
     bf16x8 pf[NX][NT / 2];
-
-    // A: band MFMA of block x (run band tiles 1-h .. 5-h) and skew into LDS
-    auto stage_a = [&](auto X) {
-        constexpr int x = decltype(X)::value;
-        constexpr int h = x & 1;
-        float *skw = t.skw;
-        const bf16x8 *qv = st.qv[x];
-        const float m = st.mneg[x];
-        f32x4 cin[NBT];
-        if constexpr (MASKED) {
-            // band row 16 bt + 4 g + v is visible iff tlo <= row <= thi
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * bt + 4 * g + v;
-                    cin[bt][v] = (row > bk[x].thi || row < bk[x].tlo) ? -INFINITY : m;
-                }
-        } else {
-            const f32x4 m4 = {m, m, m, m};
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) cin[bt] = m4;
-        }
-        f32x4 acc[NBT];
-#pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + 1 - h][0], qv[0], cin[bt]);
-#pragma unroll
-        for (int kk = 1; kk < NKK; ++kk)
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) acc[bt] = mfma(rf[bt + 1 - h][kk], qv[kk], acc[bt]);
-        lds_order();
-#pragma unroll
-        for (int bt = 0; bt < NBT; ++bt)   // band row cc = 16 bt + 4 g + v of query n -> column cc + n + 1
-            lds_store4(skw + lo.sst + 16 * bt, acc[bt]);
-        lds_order();
-    };
-    // B: content MFMA of block x on top of the skewed band values
-    auto stage_b = [&](auto X) {
-        constexpr int x = decltype(X)::value;
-        const float *skw = t.skw;
-        f32x4 cin[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-            cin[tt] = *reinterpret_cast<const f32x4 *>(skw + lo.sld + 16 * tt);
-        lds_order();
-        if (LOWER && MASKED) {
-            // keys below kmem are hidden from every query of the block
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (16 * tt + 4 * g + v < bk[x].kmem) cin[tt][v] = -INFINITY;
-        }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 acc = cin[tt];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = mfma(kf[tt][kk], st.qu[x][kk], acc);
-            sc[x][tt] = acc;
-        }
-    };
-    // C: overflow check (rare rescale), probabilities as bf16 B fragments
-    auto stage_c = [&](auto X) {
+    // overflow check (rare rescale), probabilities as bf16 B fragments
+    auto softmax = [&](auto X) {
         constexpr int x = decltype(X)::value;
         float mx = max3(sc[x][0][0], sc[x][0][1], sc[x][0][2]);
         mx = max3(mx, sc[x][0][3], sc[x][1][0]);
@@ -359,8 +410,8 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
             pf[x][ch] = __builtin_convertvector(p8, bf16x8);
         }
     };
-    // D: O^T += V^T . P^T, denominator += ones . P^T
-    auto stage_d = [&](auto X) {
+    // O^T += V^T . P^T, denominator += ones . P^T
+    auto pv = [&](auto X) {
         constexpr int x = decltype(X)::value;
 #pragma unroll
         for (int ch = 0; ch < NT / 2; ++ch) {
@@ -370,22 +421,21 @@ __device__ __forceinline__ void tile_body(State &st, const Tile &t, const Blk (&
         }
     };
 
-    // Pipeline over the two blocks (one skew buffer: block 1's band goes in
-    // after block 0's content stage has read it back; K and V fragments are
-    // never live together).  The scheduling barriers keep the stage order.
-    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    load_r();
-    stage_a(IC<0>{});
-    stage_b(IC<0>{});
-    fence();
-    stage_a(IC<1>{});
-    stage_c(IC<0>{});
-    stage_b(IC<1>{});
-    fence();
+    softmax(IC<0>{});
     load_v();
-    stage_d(IC<0>{});
-    stage_c(IC<1>{});
-    stage_d(IC<1>{});
+    pv(IC<0>{});
+    if constexpr (NX > 1) {
+        softmax(IC<1>{});
+        pv(IC<1>{});
+    }
+}
+
+template <bool LOWER, bool MASKED, int NX>
+__device__ __forceinline__ void tile_body(State<NX> &st, const Tile &t, const Blk (&bk)[NX], int g, const LaneOff &lo)
+{
+    f32x4 sc[NX][NT];
+    tile_h1<LOWER, MASKED, NX>(st, t, bk, g, lo, sc);
+    tile_h2<LOWER, NX>(st, t, lo, sc);
 }
 
 // ---------------------------------------------------------------------------
@@ -445,11 +495,13 @@ __device__ __forceinline__ void copy_rows(KFusedCopy *c, const CopyPos &p, __amd
     dst = make_rsrc(c->dst + p.b * c->new_bs + (int64_t)p.t * rb, (uint32_t)rb);
 }
 
-template <bool LOWER>
-__global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
+template <bool LOWER, int XW>
+__global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 {
+    using S = Split<XW>;
+    constexpr int NX = S::NX, NW = S::NW, RUNQ = S::RUNQ, PAIRS = S::PAIRS;
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 sv[3][TILE_CH];   // three: a wave's H2 may run past the barrier
     __shared__ __attribute__((aligned(16))) u32x4 sr[2][RQ * TILE_CH];
     __shared__ __attribute__((aligned(16))) float sskew[NW][SKEW];
     __shared__ __attribute__((aligned(16))) u32x4 scopy[NW][64];   // one staged Tail_M chunk per wave
@@ -471,7 +523,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     const int b = bh / a.H, h = bh - b * a.H;
     const int L = a.L, M = a.M, K = a.K;
 
-    // runs of 32 queries, paired from both ends
+    // runs of RUNQ queries, paired from both ends
     const int nr = (L + RUNQ - 1) / RUNQ;
     const int npair = (nr + 1) / 2;
     const int p0 = PAIRS * grp;
@@ -488,12 +540,12 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     if (LOWER) kt0 = max(kt0, key_lo(a, b, RUNQ * p0) / BK);
     const int kt1 = min(ntile, split * a.tiles_per_split + a.tiles_per_split);
 
-    // this wave's run: waves w and w + 4 (one SIMD) take runs p and nr - 1 - p
-    // of pair p = p0 + w % 4 (one run if they coincide)
-    const int end = wave >> 2;
-    const int p = p0 + (wave & 3);
+    // this wave's run: waves w and w + PAIRS (one SIMD) take runs p and
+    // nr - 1 - p of pair p = p0 + w % PAIRS (one run if they coincide)
+    const int end = wave / PAIRS;
+    const int p = p0 + wave % PAIRS;
     const int run = end == 0 ? p : nr - 1 - p;
-    const bool run_ok = (wave & 3) < np && (end == 0 || nr - 1 - p > p);
+    const bool run_ok = wave % PAIRS < np && (end == 0 || nr - 1 - p > p);
     int i0[NX];
 #pragma unroll
     for (int x = 0; x < NX; ++x) i0[x] = RUNQ * run + 16 * x;
@@ -514,41 +566,36 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         kmem_abs = M - mv;
     }
 
-    // ---- direct loads: thread tid moves chunks tid and tid + 256 of each tile
-    // (rows tid / 8 and tid / 8 + 32), reading the chunk the XOR swizzle puts at
-    // that LDS position.  Rows outside [0, K) read zeros.
-    const int lrow = (unsigned)tid / CPR;
+    // ---- direct loads.  Each 8 KB tile (K, V, one r ring quarter) is eight
+    // 1 KB blocks, one per loading wave: K and r fragment block w (16-row
+    // block w / 2, k-step w % 2; see frag_src), V rows 8 w .. 8 w + 7 with the
+    // chunk the V swizzle puts at each LDS position.  With eight waves every
+    // wave loads a block of each; with sixteen, waves 0-7 load K and ring 0,
+    // waves 8-15 V and ring 1.  Rows outside [0, K) read zeros.
+    const int lw = wave & 7;                       // block this wave loads
+    const int lrow = 8 * lw + (lane >> 3);         // V row of this lane's chunk
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
-    const int kch = ((tid & (CPR - 1)) ^ swz_k(lrow)) * 16;
-    const int vch = ((tid & (CPR - 1)) ^ swz_v(lrow)) * 16;
     const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
-    const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][wave * 64]));
-    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][wave * 64]));
-    const uint32_t sr0_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0][wave * 64]));
-    const uint32_t sr1_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[1][wave * 64]));
+    const int fsrc_k = (16 * (lw >> 1)) * krow_b + frag_src(lane, lw & 1, krow_b);
+    const int fsrc_r = (16 * (lw >> 1)) * rrow_b + frag_src(lane, lw & 1, rrow_b);
+    const int vsrc = lrow * vrow_b + ((lane & (CPR - 1)) ^ swz_v(lrow)) * 16;
+    const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][lw * 64]));
+    const uint32_t sv_base = __builtin_amdgcn_readfirstlane(lds_addr(&sv[0][lw * 64]));
+    const uint32_t sr0_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[0][lw * 64]));
+    const uint32_t sr1_base = __builtin_amdgcn_readfirstlane(lds_addr(&sr[1][lw * 64]));
+    const bool load_k = NW == 8 || wave < 8;      // K and ring 0
+    const bool load_v = NW == 8 || wave >= 8;     // V and ring 1
     auto load_kv = [&](int kt) {
-        const uint32_t boff = (uint32_t)(kt & 1) * (TILE_CH * 16);
-#pragma unroll
-        for (int e = 0; e < LPT; ++e) {
-            const int row = kt * BK + lrow + e * (NTHR / CPR);
-            const uint32_t loff = boff + (uint32_t)e * (NTHR * 16);
-            load_lds16(krs, (uint32_t)(row * krow_b + kch), sk_base + loff);
-            load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + loff);
-        }
+        if (load_k) load_lds16(krs, (uint32_t)(kt * BK * krow_b + fsrc_k), sk_base + (uint32_t)(kt & 1) * (TILE_CH * 16));
+        if (load_v) load_lds16(vrs, (uint32_t)(kt * BK * vrow_b + vsrc), sv_base + (uint32_t)(kt % 3) * (TILE_CH * 16));
     };
-    // ring quarter q % RQ holds r rows cb + 64 q .. +63 (the swizzle only
-    // depends on the row within the quarter)
+    // ring quarter q % RQ holds r rows cb + 64 q .. +63
     auto load_r_quarter = [&](int q) {
         const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
-#pragma unroll
-        for (int e = 0; e < LPT; ++e) {
-            const int x = 64 * q + lrow + e * (NTHR / CPR);
-            const uint32_t loff = qoff + (uint32_t)e * (NTHR * 16);
-            load_lds16(rrs, (uint32_t)((cb0 + x) * rrow_b + kch), sr0_base + loff);
-            load_lds16(rrs, (uint32_t)((cb1 + x) * rrow_b + kch), sr1_base + loff);
-        }
+        if (load_k) load_lds16(rrs, (uint32_t)((cb0 + 64 * q) * rrow_b + fsrc_r), sr0_base + qoff);
+        if (load_v) load_lds16(rrs, (uint32_t)((cb1 + 64 * q) * rrow_b + fsrc_r), sr1_base + qoff);
     };
 
     if (kt0 < kt1) {
@@ -556,7 +603,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
 #pragma unroll
         for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
     }
-    State st;
+    State<NX> st;
     // ---- query fragments: c (q + u) and c (q + vb), in fp32, rounded once to bf16
     // (their loads go out after the first tile's, so the two latencies overlap)
     const QBias qb = load_qbias(up, wp, g);
@@ -576,6 +623,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
     __syncthreads();
 
     const LaneOff lo = lane_offsets(g, n);
+    f32x4 sc[NX][NT];   // scores of the current tile, from H1 to H2
     Tile t;
     t.sr = sr[end];
     t.skw = sskew[wave];
@@ -641,7 +689,13 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         }
     };
 
-    // one key tile: stage the next tile, compute this one, wait
+    // One key tile: stage the next tile, compute H1 of this one, wait for the
+    // staged loads and meet the workgroup, then H2.  A wave's H2 of tile kt
+    // runs while other waves start tile kt + 1 and its loads land: K and the
+    // r ring are only read in H1, V has three buffers (tile kt + 2 loads into
+    // the one tile kt - 1 used).  Taking the barrier between the halves
+    // measured faster (37.0 us at B8 H16 L512 M512) than after them (38.4 us)
+    // or than half of the waves taking it at each point (39.5 us).
     auto step = [&](auto ACT, auto MC, int kt) {
         constexpr bool ACTIVE = decltype(ACT)::value != 0;
         constexpr bool MASKED = decltype(MC)::value != 0;
@@ -670,13 +724,14 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
                 bk[x].kmem = kmem_abs - j0;
             }
             t.sk = sk[kt & 1];
-            t.sv = sv[kt & 1];
+            t.sv = sv[kt % 3];
             t.kt = kt;
             t.first = (kt == kt0);
-            tile_body<LOWER, MASKED>(st, t, bk, g, lo);
+            tile_h1<LOWER, MASKED, NX>(st, t, bk, g, lo, sc);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
+        if constexpr (ACTIVE) tile_h2<LOWER, NX>(st, t, lo, sc);
     };
     // Walk the tiles in segments of one kind (active, masks needed) so that
     // each loop runs one instance of the tile body and the state stays in place.
@@ -696,7 +751,7 @@ __global__ __launch_bounds__(NTHR) void relattn_fwd_bf16_kernel(RelAttnArgs a)
         }
     }
 
-    // the last staged chunk has landed (every tile ends with a full wait)
+    // the last staged chunk has landed (every tile has a full wait before its barrier)
     copy_out();
     if (fused_copy_args()->nchunks > 0) {
         for (; pos.b < fused_copy_args()->B; copy_advance(fused_copy_args(), pos)) {
@@ -755,6 +810,7 @@ constexpr int SNW = 4;   // waves per streaming workgroup at most
 
 __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnArgs a)
 {
+    constexpr int NX = Split<2>::NX, RUNQ = Split<2>::RUNQ;
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sr[RQ * TILE_CH];
@@ -804,7 +860,6 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)(((int64_t)(K - 1) * a.ks[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)(((int64_t)(K - 1) * a.vs[2] + DH) * 2));
     const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rp, (uint32_t)(((int64_t)(K - 1) * a.rs[1] + DH) * 2));
-    const int kch0 = ((lane & (CPR - 1)) ^ swz_k(lr)) * 16, kch1 = ((lane & (CPR - 1)) ^ swz_k(lr + 8)) * 16;
     const int vch = ((lane & (CPR - 1)) ^ swz_v(lr)) * 16;
     const int krow_b = (int)a.ks[2] * 2, vrow_b = (int)a.vs[2] * 2, rrow_b = (int)a.rs[1] * 2;
     const uint32_t sk_base = __builtin_amdgcn_readfirstlane(lds_addr(&sk[0][0]));
@@ -818,16 +873,17 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
         for (int blk = wave; blk < TILE_CH / 64; blk += nw) {
             const int row = kt * BK + 8 * blk + lr;
             const uint32_t loff = boff + (uint32_t)blk * 1024u;
-            load_lds16(krs, (uint32_t)(row * krow_b + ((blk & 1) ? kch1 : kch0)), sk_base + loff);
+            // K: fragment block blk (16-row block blk / 2, k-step blk % 2); V: rows 8 blk .. + 7
+            const int ksrc = (kt * BK + 16 * (blk >> 1)) * krow_b + frag_src(lane, blk & 1, krow_b);
+            load_lds16(krs, (uint32_t)ksrc, sk_base + loff);
             load_lds16(vrs, (uint32_t)(row * vrow_b + vch), sv_base + loff);
         }
     };
     auto load_r_quarter = [&](int q) {
         const uint32_t qoff = (uint32_t)(q & (RQ - 1)) * (TILE_CH * 16);
         for (int blk = wave; blk < TILE_CH / 64; blk += nw) {
-            const int x = 64 * q + 8 * blk + lr;
-            load_lds16(rrs, (uint32_t)((cb + x) * rrow_b + ((blk & 1) ? kch1 : kch0)),
-                       sr_base + qoff + (uint32_t)blk * 1024u);
+            const int rsrc = (cb + 64 * q + 16 * (blk >> 1)) * rrow_b + frag_src(lane, blk & 1, rrow_b);
+            load_lds16(rrs, (uint32_t)rsrc, sr_base + qoff + (uint32_t)blk * 1024u);
         }
     };
     // the first tile's loads go out before the query fragments' (they do not
@@ -838,7 +894,7 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
         for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
     }
 
-    State st;
+    State<NX> st;
     const QBias qb = load_qbias(up, wp, g);
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
@@ -882,8 +938,8 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
             t.sv = sv[kt & 1];
             t.kt = kt;
             t.first = (kt == kt0);
-            if (kt >= ue) tile_body<false, true>(st, t, bk, g, lo);
-            else tile_body<false, false>(st, t, bk, g, lo);
+            if (kt >= ue) tile_body<false, true, NX>(st, t, bk, g, lo);
+            else tile_body<false, false, NX>(st, t, bk, g, lo);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
@@ -921,16 +977,20 @@ __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnAr
 
 }  // namespace
 
+// Work split of the throughput kernel (16-query blocks per wave).
+constexpr int FWD_XW = 2;
+
 int relattn_bf16_groups_per_head(int L)
 {
-    const int nr = (L + RUNQ - 1) / RUNQ;
+    using S = Split<FWD_XW>;
+    const int nr = (L + S::RUNQ - 1) / S::RUNQ;
     const int npair = (nr + 1) / 2;
-    return (npair + PAIRS - 1) / PAIRS;
+    return (npair + S::PAIRS - 1) / S::PAIRS;
 }
 
 bool relattn_bf16_supported(int dh) { return dh == DH; }
 
-int relattn_bf16_stream_runs(int L) { return (L + RUNQ - 1) / RUNQ; }
+int relattn_bf16_stream_runs(int L) { return (L + Split<2>::RUNQ - 1) / Split<2>::RUNQ; }
 
 hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t s)
 {
@@ -945,20 +1005,21 @@ hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t 
 hipError_t launch_relattn_bf16(const RelAttnArgs &args, int dh, hipStream_t s)
 {
     if (dh != DH) return hipErrorInvalidValue;
+    using S = Split<FWD_XW>;
     const int blocks = args.nqb * args.B * args.H * args.nsplit;
     RelAttnArgs a = args;
     if (a.cp.nchunks > 0) {
         // a wave's next chunk is the launch's wave count further on
-        const int64_t waves = (int64_t)blocks * NW, cpb = (int64_t)a.cp.M_new * a.cp.cpr;
+        const int64_t waves = (int64_t)blocks * S::NW, cpb = (int64_t)a.cp.M_new * a.cp.cpr;
         const int64_t rem = waves % cpb;
         a.cp.inc_b = (int)std::min<int64_t>(waves / cpb, a.cp.B);
         a.cp.inc_t = (int)(rem / a.cp.cpr);
         a.cp.inc_ch = (int)(rem % a.cp.cpr);
     }
     if (a.window > 0 || a.mem_valid)
-        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<true>, dim3(blocks), dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((relattn_fwd_bf16_kernel<true, FWD_XW>), dim3(blocks), dim3(S::NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(relattn_fwd_bf16_kernel<false>, dim3(blocks), dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((relattn_fwd_bf16_kernel<false, FWD_XW>), dim3(blocks), dim3(S::NTHR), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_relattn_combine(a, 1, dh, s);
