@@ -650,11 +650,11 @@ __global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAt
 
     // Tail_M chunks of this wave: inside the key loop one every cstride tiles
     // (the copy steps, staggered over the workgroup's waves so that the copy's
-    // traffic is spread over the loop), staged in LDS by a direct load in one
-    // copy step and written out at the start of the next (after the wait and
-    // barrier that end every tile), so the copy holds no vector registers
-    // across the tile body; the rest after the loop.  pos is the staged chunk
-    // while one is staged, else the next to load.
+    // traffic is spread over the loop), staged in LDS by a direct load after
+    // the barrier of a copy step and written out after the next tile's wait
+    // and barrier, so the copy holds no vector registers across the tile body;
+    // the rest after the loop.  pos is the staged chunk while one is staged,
+    // else the next to load.
     CopyPos pos{0x7fffffff, 0, 0};    // past the last batch row: no copy
     if (fused_copy_args()->nchunks > 0) pos = copy_first(fused_copy_args(), (int)blockIdx.x * NW + wave);
     bool staged = false;
@@ -700,16 +700,6 @@ __global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAt
         constexpr bool ACTIVE = decltype(ACT)::value != 0;
         constexpr bool MASKED = decltype(MC)::value != 0;
         const int j0 = kt * BK;
-        if (ccount-- == 0) {       // a copy step of this wave
-            ccount = cstride - 1;
-            copy_out();
-            if (pos.b < fused_copy_args()->B) {
-                __amdgpu_buffer_rsrc_t src, dst;
-                copy_rows(fused_copy_args(), pos, src, dst);
-                load_lds16(src, 1024u * pos.ch + lane16(), scopy_base);
-                staged = true;
-            }
-        }
         if (kt + 1 < kt1) {
             load_kv(kt + 1);
             load_r_quarter(kt + RQ - 1);
@@ -731,6 +721,19 @@ __global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAt
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
         __syncthreads();
+        // The chunk staged in the previous copy step has landed: write it out
+        // and stage the next one, whose load then has this H2 and the next H1
+        // to land before the wait.
+        copy_out();
+        if (ccount-- == 0) {       // a copy step of this wave
+            ccount = cstride - 1;
+            if (pos.b < fused_copy_args()->B) {
+                __amdgpu_buffer_rsrc_t src, dst;
+                copy_rows(fused_copy_args(), pos, src, dst);
+                load_lds16(src, 1024u * pos.ch + lane16(), scopy_base);
+                staged = true;
+            }
+        }
         if constexpr (ACTIVE) tile_h2<LOWER, NX>(st, t, lo, sc);
     };
     // Walk the tiles in segments of one kind (active, masks needed) so that
@@ -751,7 +754,7 @@ __global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAt
         }
     }
 
-    // the last staged chunk has landed (every tile has a full wait before its barrier)
+    __builtin_amdgcn_s_waitcnt(0);   // the last staged chunk has landed
     copy_out();
     if (fused_copy_args()->nchunks > 0) {
         for (; pos.b < fused_copy_args()->B; copy_advance(fused_copy_args(), pos)) {
