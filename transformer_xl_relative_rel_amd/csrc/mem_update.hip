@@ -21,9 +21,13 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;      // 16-byte words per thread
 
 // grid: x over the 16-byte words of one batch row's new memory, y over
-// (buffer, batch row).  Every load of a thread is issued before its stores;
-// both are non-temporal (streamed once, the new memory is next read a whole
-// segment later).
+// (buffer, batch row).  Every load of a thread is issued before its stores.
+// The stores are non-temporal (the new memory is next read a whole segment
+// later); the loads are plain, so a source the previous step left in the
+// last-level cache is read from there (17 buffers of [4, 512, 1024] bf16:
+// 21.7 us with plain loads against 24.4 us with non-temporal ones; on copies
+// of several GB, which no longer fit that cache, non-temporal loads are ~5%
+// faster).
 __global__ __launch_bounds__(kThreads) void mem_update_kernel(MemUpdateArgs a)
 {
     const int buf = (int)blockIdx.y / a.B;
@@ -35,16 +39,30 @@ __global__ __launch_bounds__(kThreads) void mem_update_kernel(MemUpdateArgs a)
     const uint32_t rc = (uint32_t)a.row_chunks;
     const uint32_t e0 = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
     u32x4 val[kUnroll];
+    // When every row of the new memory comes from one source (all of it from
+    // h, as in a stack whose memory length equals the segment length, or all
+    // from mem), the chunks are contiguous in that source and need no row split.
+    const unsigned char *one = nullptr;
+    if (a.beg >= a.M_cur) one = hh + (int64_t)(a.beg - a.M_cur) * rc * 16;
+    else if (a.beg + a.M_new <= a.M_cur) one = mem + (int64_t)a.beg * rc * 16;
+    if (one) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t e = e0 + u * kThreads;
-        if (e < per_batch) {
-            const uint32_t t = e / rc;                  // row of the new memory
-            const uint32_t c = e - t * rc;
-            const int src_row = a.beg + (int)t;         // row of cat([mem; h])
-            const unsigned char *src = (src_row < a.M_cur) ? mem + ((int64_t)src_row * rc + c) * 16
-                                                           : hh + ((int64_t)(src_row - a.M_cur) * rc + c) * 16;
-            val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t e = e0 + u * kThreads;
+            if (e < per_batch) val[u] = *reinterpret_cast<const u32x4 *>(one + (int64_t)e * 16);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t e = e0 + u * kThreads;
+            if (e < per_batch) {
+                const uint32_t t = e / rc;                  // row of the new memory
+                const uint32_t c = e - t * rc;
+                const int src_row = a.beg + (int)t;         // row of cat([mem; h])
+                const unsigned char *src = (src_row < a.M_cur) ? mem + ((int64_t)src_row * rc + c) * 16
+                                                               : hh + ((int64_t)(src_row - a.M_cur) * rc + c) * 16;
+                val[u] = *reinterpret_cast<const u32x4 *>(src);
+            }
         }
     }
 #pragma unroll
