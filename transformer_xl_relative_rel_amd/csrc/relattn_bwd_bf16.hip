@@ -514,18 +514,14 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
         // Each phase has an unmasked instance for the steps (and waves) that
         // need no mask, chosen by a wave-uniform branch.
         const int pw = L - 1 - (i0 + QS - 1) + j0;
+        // The band tiles come out transposed (band columns 4g..4g+3 of query n in
+        // lane (g, n)), so each lane writes its four columns with one 16-byte store.
         auto band = [&](auto mtag) {
             constexpr bool MASKED = decltype(mtag)::value;
             const bf16x8 qa0 = row_frag_at(tqv + s2 * BLK16B, rlo0);
             const bf16x8 qa1 = row_frag_at(tqv + s2 * BLK16B, rlo1);
-            f32x4 nl;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) nl[v] = -sl2[buf][16 * s2 + 4 * g + v];
-            if (MASKED) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (i0 + 16 * s2 + 4 * g + v >= L) nl[v] = -INFINITY;
-            }
+            float nl = -sl2[buf][16 * s2 + n];
+            if (MASKED && i0 + 16 * s2 + n >= L) nl = -INFINITY;
             bf16x8 rb[TPW][2];
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
@@ -538,18 +534,20 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
             f32x4 acc[TPW];
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
-                f32x4 cin = nl;
+                f32x4 cin = f32x4{nl, nl, nl, nl};
                 if (MASKED) {
-                    const int pc = pw + 16 * (pt0 + u) + n;      // this lane's r row
-                    if (pc > K - 1 || (win > 0 && pc < K - win)) cin = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int pc = pw + 16 * (pt0 + u) + 4 * g + v;      // r row of element v
+                        if (pc > K - 1 || (win > 0 && pc < K - win)) cin[v] = -INFINITY;
+                    }
                 }
-                acc[u] = mfma(qa0, rb[u][0], cin);
-                acc[u] = mfma(qa1, rb[u][1], acc[u]);
+                acc[u] = mfma(rb[u][0], qa0, cin);
+                acc[u] = mfma(rb[u][1], qa1, acc[u]);
             }
 #pragma unroll
             for (int u = 0; u < TPW; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) tband[(16 * s2 + 4 * g + v) * TS + 16 * (pt0 + u) + n] = acc[u][v];
+                *reinterpret_cast<f32x4 *>(&tband[(16 * s2 + n) * TS + 16 * (pt0 + u) + 4 * g]) = acc[u];
         };
         // masking needed: rows past L, r rows past K-1 (causal) or below K - window
         const bool qmask = i0 + QS > L;
