@@ -419,7 +419,7 @@ def main():
         Fb = flops_bwd(B, H, L, M, dh)
         bwd = {"ms_per_call": round(bwd_ms, 5), "tflops_alg": round(Fb / (bwd_ms * 1e-3) / 1e12, 2),
                "pct_bf16_peak": round(100.0 * Fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-               "flops_per_call": Fb, "kernels": "prep, dq, dkv, dr, bias (txl_relattn_bwd)"}
+               "flops_per_call": Fb, "kernels": "prep, dkv, dq, dr (txl_relattn_bwd)"}
     F = flops_alg(B, H, L, M, dh)
     value = F / (ms_step * 1e-3) / 1e12
     achieved = F / (attn_ms * 1e-3) / 1e12

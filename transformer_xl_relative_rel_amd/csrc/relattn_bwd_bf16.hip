@@ -16,7 +16,7 @@
 //   dr_c = scale sum over b and (i, j) with L-1-i+j = c of dS_ij (q_i + vb)
 //   du = sum over b, i of the k part of dq_i, dvb = the same of its r part.
 //
-// Kernels (one stream, in the order prep, dkv, dq, dr, bias):
+// Kernels (one stream, in the order prep, dkv, dq, dr):
 //   prep : c (q + u) and c (q + vb) rounded to bf16 exactly as the forward
 //          forms its query operands (c = scale log2 e), D_i, lse in log2 units.
 //   dkv  : one workgroup per 128 keys (4 waves of 32 keys), queries in steps
@@ -37,8 +37,9 @@
 //          (row i shifted by L-1-i: aligned words and a byte shift), and
 //          dq^T += R_band^T . G^T reads the same rows at band positions.  Per
 //          16-query sums of both parts go to the workspace for du and dvb.
-//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r).
-//   bias : du, dvb from the per-block sums, in a fixed order.
+//   dr   : dr[h] = sum_b G_b^T . c (q + vb)_b (one workgroup per 64 rows of r);
+//          the head's first two workgroups then sum du and dvb from the
+//          per-block sums in a fixed order.
 // No atomics: every output element has one writer and a fixed summation
 // order, so results are bitwise reproducible.
 
@@ -660,6 +661,28 @@ __global__ __launch_bounds__(KTHR) void bwd_dkv_kernel(RelAttnBwdArgs a)
 // four batch groups stage their own 64-query steps, prefetched two steps ahead
 // in registers, and their sums are added in group order at the end.
 
+// du, dvb (which = 0, 1) of head h from the per-16-query sums dq stored: 16
+// waves each summing every 16th block of every (split, batch row), then the 16
+// wave sums in wave order.  Called by a whole 16-wave workgroup.
+__device__ __forceinline__ void bias_sums(const RelAttnBwdArgs &a, int h, int which, float (&red)[16][DH])
+{
+    const int t = threadIdx.x, wave = t >> 6, d = t & 63;
+    float s = 0.f;
+    for (int sb = 0; sb < a.nsplit * a.B; ++sb) {       // (split, b) in order; blocks k = wave (mod 16)
+        const int sp = sb / a.B, b = sb - sp * a.B;
+        const float *pp = a.bias_part + ((int64_t)sp * a.B * a.H + b * a.H + h) * a.nqblk * (2 * DH) + which * DH + d;
+#pragma unroll 2
+        for (int k = wave; k < a.nqblk; k += 16) s += pp[(int64_t)k * 2 * DH];
+    }
+    red[wave][d] = s;
+    __syncthreads();
+    if (wave == 0) {
+        float tot = 0.f;
+        for (int w = 0; w < 16; ++w) tot += red[w][d];
+        (which ? a.dvb : a.du)[h * DH + d] = tot;
+    }
+}
+
 constexpr int RW = 16;
 constexpr int RG = 4;               // batch groups
 constexpr int RQS = 64;             // queries per step
@@ -669,6 +692,7 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     __shared__ __attribute__((aligned(16))) u32x4 sg[RG][RQS * CPR];
     __shared__ __attribute__((aligned(16))) u32x4 sq[RG][RQS * CPR];
     __shared__ __attribute__((aligned(16))) f32x4 red[RG - 1][4 * NDT * 64];
+    __shared__ float bred[16][DH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -787,28 +811,12 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
             }
         }
     }
-}
-
-// du, dvb: the per-block partial sums of one head, 16 waves each summing every
-// 16th block of every (split, batch row), then the 16 wave sums in wave order.
-__global__ __launch_bounds__(1024) void bwd_bias_kernel(RelAttnBwdArgs a)
-{
-    __shared__ float red[16][DH];
-    const int h = blockIdx.x >> 1, which = blockIdx.x & 1;
-    const int t = threadIdx.x, wave = t >> 6, d = t & 63;
-    float s = 0.f;
-    for (int sb = 0; sb < a.nsplit * a.B; ++sb) {       // (split, b) in order; blocks k = wave (mod 16)
-        const int sp = sb / a.B, b = sb - sp * a.B;
-        const float *pp = a.bias_part + ((int64_t)sp * a.B * a.H + b * a.H + h) * a.nqblk * (2 * DH) + which * DH + d;
-#pragma unroll 2
-        for (int k = wave; k < a.nqblk; k += 16) s += pp[(int64_t)k * 2 * DH];
-    }
-    red[wave][d] = s;
-    __syncthreads();
-    if (wave == 0) {
-        float tot = 0.f;
-        for (int w = 0; w < 16; ++w) tot += red[w][d];
-        (which ? a.dvb : a.du)[h * DH + d] = tot;
+    // du and dvb of the head on its first two column blocks, which have the
+    // fewest steps (the per-16-query sums were stored by dq, launched before)
+    if (kbi < 2) bias_sums(a, h, kbi, bred);
+    if (nkb == 1) {
+        __syncthreads();
+        bias_sums(a, h, 1, bred);
     }
 }
 
@@ -905,7 +913,6 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
     if (a.nsplit > 1)
         hipLaunchKernelGGL(bwd_dq_combine_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(bwd_dr_kernel, dim3((unsigned)(a.H * ((a.K + BK - 1) / BK))), dim3(64 * RW), 0, s, a);
-    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(2 * a.H)), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
