@@ -154,12 +154,15 @@ __device__ __forceinline__ const TXL_LDS_AS char *lds_bytes(const u32x4 *tile)
     return (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)tile;
 }
 
-// Four floats to consecutive LDS words as four one-word stores.  Left alone the
-// compiler merges them into two-word stores (ds_write2_b32), which measured
-// about 10% slower in the forward kernel for the skew rows' lane pattern.
+// Four floats to consecutive LDS words (4-byte aligned only).  The compiler
+// pairs them into two-word stores (ds_write2_b32, half the store instructions);
+// in the current forward kernel that measured 3.5% faster than four one-word
+// stores (37.1 vs 38.4 us at B8 H16 L512 M512) and freed the registers its
+// unmasked instance had spilled.  (An earlier build of the kernel measured the
+// opposite, ~10% slower.)
 __device__ __forceinline__ void lds_store4(float *dst, f32x4 v)
 {
-    volatile TXL_LDS_AS float *p = (volatile TXL_LDS_AS float *)dst;
+    TXL_LDS_AS float *p = (TXL_LDS_AS float *)dst;
     p[0] = v[0];
     p[1] = v[1];
     p[2] = v[2];
