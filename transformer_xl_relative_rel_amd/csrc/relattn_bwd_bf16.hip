@@ -71,6 +71,26 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 template <bool B> struct BoolC { static constexpr bool value = B; };   // compile-time flag for generic lambdas
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Sums over groups of lanes by DPP moves on the VALU (no LDS traffic): swaps
+// within quads (lane distance 1, then 2), the half-row mirror (pairs the two
+// quads of each 8 lanes) and the row mirror (pairs the two halves of each 16).
+// Every lane adds the same two partial sums as an xor butterfly would, so the
+// results are the butterfly's bit for bit.
+template <int CTRL> __device__ __forceinline__ float dpp_add(float x)
+{
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float x)      // lanes 8k .. 8k + 7
+{
+    x = dpp_add<0xb1>(x);       // quad_perm [1, 0, 3, 2]
+    x = dpp_add<0x4e>(x);       // quad_perm [2, 3, 0, 1]
+    return dpp_add<0x141>(x);   // row_half_mirror
+}
+__device__ __forceinline__ float sum16(float x)     // lanes 16k .. 16k + 15
+{
+    return dpp_add<0x140>(sum8(x));   // row_mirror
+}
+
 // ---------------------------------------------------------------------------
 // prep: 32 rows per 256-thread workgroup, 8 threads (16 bytes each) per row.
 
@@ -105,9 +125,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
         for (int e = 0; e < 8; ++e)
             dsum += bf16_val((o[e >> 1] >> (16 * (e & 1))) & 0xffffu) * bf16_val((d[e >> 1] >> (16 * (e & 1))) & 0xffffu);
     }
-    dsum += __shfl_xor(dsum, 1);
-    dsum += __shfl_xor(dsum, 2);
-    dsum += __shfl_xor(dsum, 4);
+    dsum = sum8(dsum);
     if (ok && part == 0) {
         a.dd[rr] = dsum;
         a.lse2[rr] = a.lse[rr] * LOG2E;
@@ -352,12 +370,7 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                float su = dqu[dt][v] * scale, sw = dqv[dt][v] * scale;
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    su += __shfl_xor(su, o);
-                    sw += __shfl_xor(sw, o);
-                }
+                const float su = sum16(dqu[dt][v] * scale), sw = sum16(dqv[dt][v] * scale);
                 if (n == 0) {
                     part[16 * dt + 4 * g + v] = su;
                     part[DH + 16 * dt + 4 * g + v] = sw;
