@@ -702,10 +702,13 @@ constexpr int RQS = 64;             // queries per step
 
 __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
 {
-    __shared__ __attribute__((aligned(16))) u32x4 sg[RG][RQS * CPR];
-    __shared__ __attribute__((aligned(16))) u32x4 sq[RG][RQS * CPR];
-    __shared__ __attribute__((aligned(16))) f32x4 red[RG - 1][4 * NDT * 64];
+    // two staging buffers per batch group, so that one barrier per step suffices;
+    // the batch groups' sums meet in the G buffers after the loop
+    __shared__ __attribute__((aligned(16))) u32x4 sg[2][RG][RQS * CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 sq[2][RG][RQS * CPR];
     __shared__ float bred[16][DH];
+    static_assert(sizeof(sg) >= (RG - 1) * 4 * NDT * 64 * sizeof(f32x4), "the group sums fit in the G buffers");
+    TXL_LDS_AS f32x4 *red = (TXL_LDS_AS f32x4 *)(TXL_LDS_AS void *)&sg[0][0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -784,30 +787,32 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
     Fetch fa, fb;
     if (nsteps > 0) fetch(0, fa);
     if (nsteps > 1) fetch(1, fb);
-    auto step = [&](int t, Fetch &f) {
-        __syncthreads();
-        sg[bg][lrow * CPR + lpos] = f.g[0] & f.keep[0];
-        sq[bg][lrow * CPR + lpos] = f.q[0];
-        sg[bg][(lrow + 32) * CPR + lpos] = f.g[1] & f.keep[1];
-        sq[bg][(lrow + 32) * CPR + lpos] = f.q[1];
+    // Step t stages into buffer t & 1, which step t - 2 read: every wave
+    // finished that before the barrier of step t - 1, which this wave has passed.
+    auto step = [&](int t, Fetch &f, int sb) {
+        sg[sb][bg][lrow * CPR + lpos] = f.g[0] & f.keep[0];
+        sq[sb][bg][lrow * CPR + lpos] = f.q[0];
+        sg[sb][bg][(lrow + 32) * CPR + lpos] = f.g[1] & f.keep[1];
+        sq[sb][bg][(lrow + 32) * CPR + lpos] = f.q[1];
         __syncthreads();
         if (t + 2 < nsteps) fetch(t + 2, f);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const TXL_LDS_AS char *tgb = lds_bytes(sg[bg]) + half * 2 * BLK16B;
-            const TXL_LDS_AS char *tqb = lds_bytes(sq[bg]) + half * 2 * BLK16B;
+            const TXL_LDS_AS char *tgb = lds_bytes(sg[sb][bg]) + half * 2 * BLK16B;
+            const TXL_LDS_AS char *tqb = lds_bytes(sq[sb][bg]) + half * 2 * BLK16B;
             const bf16x8 ga = col_frag_at(tgb, trg);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(ga, col_frag_at(tqb, trl[dt]), acc[dt]);
         }
     };
     for (int t = 0; t < nsteps; t += 2) {
-        step(t, fa);
-        if (t + 1 < nsteps) step(t + 1, fb);
+        step(t, fa, 0);
+        if (t + 1 < nsteps) step(t + 1, fb, 1);
     }
+    __syncthreads();   // every wave's last reads of the staging buffers are done
     if (bg > 0) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) red[bg - 1][(psub * NDT + dt) * 64 + lane] = acc[dt];
+        for (int dt = 0; dt < NDT; ++dt) red[((bg - 1) * 4 * NDT + psub * NDT + dt) * 64 + lane] = acc[dt];
     }
     __syncthreads();
     if (bg == 0) {
@@ -815,7 +820,7 @@ __global__ __launch_bounds__(64 * RW) void bwd_dr_kernel(RelAttnBwdArgs a)
         for (int dt = 0; dt < NDT; ++dt) {
             f32x4 sum = acc[dt];
 #pragma unroll
-            for (int k = 0; k < RG - 1; ++k) sum += red[k][(psub * NDT + dt) * 64 + lane];
+            for (int k = 0; k < RG - 1; ++k) sum += red[(k * 4 * NDT + psub * NDT + dt) * 64 + lane];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int p = p0 + 16 * psub + 4 * g + v;
