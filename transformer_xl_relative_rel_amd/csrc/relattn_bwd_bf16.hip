@@ -104,31 +104,38 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
     const int64_t rr = ok ? row : 0;
     const int bh = (int)(rr / a.L), i = (int)(rr - (int64_t)bh * a.L);
     const int b = bh / a.H, h = bh - b * a.H;
-    float dsum = 0.f;
+    float dsum = 0.f, lse = 0.f;
     if (ok) {
+        // every load first, so that a thread waits for one memory round trip
+        // (stores to qu and qv may alias out or dout as far as the compiler
+        // knows, so it would not move those loads above them)
         const uint16_t *qp = static_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1] + (int64_t)i * a.qs[2];
+        const int64_t ooff = b * a.os[0] + h * a.os[1] + (int64_t)i * a.os[2] + 8 * part;
         const u32x4 raw = *reinterpret_cast<const u32x4 *>(qp + 8 * part);
-        const float *up = a.u + h * DH + 8 * part, *wp = a.vb + h * DH + 8 * part;
+        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.out) + ooff);
+        const u32x4 d = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.dout) + ooff);
+        const f32x4 *up = reinterpret_cast<const f32x4 *>(a.u + h * DH + 8 * part);
+        const f32x4 *wp = reinterpret_cast<const f32x4 *>(a.vb + h * DH + 8 * part);
+        const f32x4 u0 = up[0], u1 = up[1], w0 = wp[0], w1 = wp[1];
+        lse = a.lse[rr];
+        __builtin_amdgcn_sched_barrier(0);   // no arithmetic (and so no wait) between the loads
         f32x8 fu, fv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = bf16_val((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-            fu[e] = (x + up[e]) * a.c;     // same operation order as the forward's query operands
-            fv[e] = (x + wp[e]) * a.c;
+            fu[e] = (x + (e < 4 ? u0[e & 3] : u1[e & 3])) * a.c;     // same operation order as the forward's query operands
+            fv[e] = (x + (e < 4 ? w0[e & 3] : w1[e & 3])) * a.c;
         }
-        *reinterpret_cast<bf16x8 *>(a.qu + rr * DH + 8 * part) = __builtin_convertvector(fu, bf16x8);
-        *reinterpret_cast<bf16x8 *>(a.qv + rr * DH + 8 * part) = __builtin_convertvector(fv, bf16x8);
-        const int64_t ooff = b * a.os[0] + h * a.os[1] + (int64_t)i * a.os[2] + 8 * part;
-        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.out) + ooff);
-        const u32x4 d = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.dout) + ooff);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             dsum += bf16_val((o[e >> 1] >> (16 * (e & 1))) & 0xffffu) * bf16_val((d[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        *reinterpret_cast<bf16x8 *>(a.qu + rr * DH + 8 * part) = __builtin_convertvector(fu, bf16x8);
+        *reinterpret_cast<bf16x8 *>(a.qv + rr * DH + 8 * part) = __builtin_convertvector(fv, bf16x8);
     }
     dsum = sum8(dsum);
     if (ok && part == 0) {
         a.dd[rr] = dsum;
-        a.lse2[rr] = a.lse[rr] * LOG2E;
+        a.lse2[rr] = lse * LOG2E;
     }
 }
 
