@@ -84,60 +84,98 @@ __global__ __launch_bounds__(256) void bias_relu_kernel(const float *x, const fl
 
 constexpr int LN_THREADS = 256;
 
+// Sum over a 256-thread workgroup, the result in every thread: DPP row sums
+// (lanes 1, 2 apart, then the half-row and row mirrors), the four rows of a
+// wave read out by lane, then the four waves through LDS.
+template <int CTRL> __device__ __forceinline__ float ln_dpp_add(float x)
+{
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float block_sum(float v, float *red)
 {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    v = ln_dpp_add<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+    v = ln_dpp_add<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+    v = ln_dpp_add<0x141>(v);   // row_half_mirror
+    v = ln_dpp_add<0x140>(v);   // row_mirror
+    const int vi = __builtin_bit_cast(int, v);
+    v = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 0)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 16))) +
+        (__builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 32)) + __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 48)));
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
-    if (lane == 0) red[w] = v;
-    __syncthreads();
-    float s = 0.f;
-    for (int i = 0; i < LN_THREADS / 64; ++i) s += red[i];
-    return s;
+    return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // out = LN(res + add + bias) * g + beta over rows of d ([SRC] nn.LayerNorm:
 // biased variance, eps).  res bf16 [N][d], add fp32 [N][d], bias fp32 [d] or
-// NULL, out bf16.  One workgroup per row; two passes (mean, then the centred
-// second moment) over values held in registers.
-constexpr int LN_MAXV = 16;   // values per thread: d <= 4096
+// NULL, out bf16; d a multiple of 4 and 16-byte aligned rows and vectors.
+// One workgroup per row; thread t holds columns 4 t + 1024 c .. + 3 for
+// chunks c, loaded before any arithmetic; two passes (mean, then the centred
+// second moment) over the values held in registers.
+constexpr int LN_CHUNKS = 4;   // d <= LN_THREADS * 4 * LN_CHUNKS = 4096
 __global__ __launch_bounds__(LN_THREADS) void add_layer_norm_kernel(const uint16_t *res, const float *add,
                                                                     const float *bias, const float *g,
                                                                     const float *beta, uint16_t *out, int d,
                                                                     float eps)
 {
-    __shared__ float red[LN_THREADS / 64];
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    __shared__ float red[2][LN_THREADS / 64];
     const int64_t row = blockIdx.x;
     const uint16_t *rp = res + row * d;
     const float *ap = add + row * d;
-    float v[LN_MAXV];
+    u32x2v rv[LN_CHUNKS];
+    f32x4v av[LN_CHUNKS], bv[LN_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < LN_CHUNKS; ++c) {
+        const int col = 4 * (threadIdx.x + c * LN_THREADS);
+        rv[c] = u32x2v{0u, 0u};
+        av[c] = bv[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        if (col < d) {
+            rv[c] = *reinterpret_cast<const u32x2v *>(rp + col);
+            av[c] = *reinterpret_cast<const f32x4v *>(ap + col);
+            if (bias) bv[c] = *reinterpret_cast<const f32x4v *>(bias + col);
+        }
+    }
+    f32x4v v[LN_CHUNKS];
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        const int col = threadIdx.x + i * LN_THREADS;
-        v[i] = 0.f;
-        if (col < d) {
-            v[i] = bf16_to_f32(rp[col]) + ap[col] + (bias ? bias[col] : 0.f);
-            s += v[i];
+    for (int c = 0; c < LN_CHUNKS; ++c) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w = rv[c][k >> 1];
+            v[c][k] = bf16_to_f32((uint16_t)((k & 1) ? (w >> 16) : (w & 0xffffu))) + av[c][k] + bv[c][k];
         }
+        s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);   // zero past d
     }
-    const float mean = block_sum(s, red) / d;
+    const float mean = block_sum(s, red[0]) / d;
     float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        const int col = threadIdx.x + i * LN_THREADS;
-        if (col < d) {
-            const float c = v[i] - mean;
-            q += c * c;
+    for (int c = 0; c < LN_CHUNKS; ++c) {
+        if (4 * (threadIdx.x + c * LN_THREADS) < d) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float x = v[c][k] - mean;
+                q += x * x;
+            }
         }
     }
-    const float var = block_sum(q, red) / d;
+    const float var = block_sum(q, red[1]) / d;
     const float inv = 1.f / sqrtf(var + eps);
     uint16_t *op = out + row * d;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        const int col = threadIdx.x + i * LN_THREADS;
-        if (col < d) op[col] = f32_to_bf16((v[i] - mean) * inv * g[col] + beta[col]);
+    for (int c = 0; c < LN_CHUNKS; ++c) {
+        const int col = 4 * (threadIdx.x + c * LN_THREADS);
+        if (col < d) {
+            const f32x4v gg = *reinterpret_cast<const f32x4v *>(g + col);
+            const f32x4v bb = *reinterpret_cast<const f32x4v *>(beta + col);
+            u32x2v o;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                o[k] = (uint32_t)f32_to_bf16((v[c][2 * k] - mean) * inv * gg[2 * k] + bb[2 * k]) |
+                       ((uint32_t)f32_to_bf16((v[c][2 * k + 1] - mean) * inv * gg[2 * k + 1] + bb[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x2v *>(op + col) = o;
+        }
     }
 }
 
@@ -149,7 +187,7 @@ int grid_for(int64_t n)
 
 }  // namespace
 
-int layer_norm_max_width() { return LN_THREADS * LN_MAXV; }
+int layer_norm_max_width() { return LN_THREADS * 4 * LN_CHUNKS; }
 
 hipError_t launch_pos_emb(uint16_t *out, int K, int d, int clamp_len, hipStream_t s)
 {
@@ -170,7 +208,7 @@ hipError_t launch_bias_relu(const float *x, const float *b, uint16_t *y, int64_t
 hipError_t launch_add_layer_norm(const uint16_t *res, const float *add, const float *bias, const float *g,
                                  const float *beta, uint16_t *out, int64_t N, int d, float eps, hipStream_t s)
 {
-    if (d > LN_THREADS * LN_MAXV || N > 0x7fffffff) return hipErrorInvalidValue;
+    if (d > LN_THREADS * 4 * LN_CHUNKS || d % 4 || N > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(add_layer_norm_kernel, dim3((unsigned)N), dim3(LN_THREADS), 0, s, res, add, bias, g, beta,
                        out, d, eps);
     return hipGetLastError();
