@@ -809,11 +809,14 @@ __global__ __launch_bounds__(Split<XW>::NTHR) void relattn_fwd_bf16_kernel(RelAt
 // registers touched 16 rows per 1 KB load and four waves fetched the same
 // tile).  The tile body is the throughput kernel's; the key splits of a head
 // are merged by the split combine.
-constexpr int SNW = 4;   // waves per streaming workgroup at most
+// Work split of the streaming kernel: STREAM_XW 16-query blocks per wave, one
+// wave per run of 16 STREAM_XW queries, so at most SNW waves for L <= 128.
+constexpr int STREAM_XW = 2;
+constexpr int SNW = 128 / Split<STREAM_XW>::RUNQ;   // waves per streaming workgroup at most
 
 __global__ __launch_bounds__(SNW * 64) void relattn_stream_bf16_kernel(RelAttnArgs a)
 {
-    constexpr int NX = Split<2>::NX, RUNQ = Split<2>::RUNQ;
+    constexpr int NX = Split<STREAM_XW>::NX, RUNQ = Split<STREAM_XW>::RUNQ;
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sv[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sr[RQ * TILE_CH];
@@ -993,7 +996,7 @@ int relattn_bf16_groups_per_head(int L)
 
 bool relattn_bf16_supported(int dh) { return dh == DH; }
 
-int relattn_bf16_stream_runs(int L) { return (L + Split<2>::RUNQ - 1) / Split<2>::RUNQ; }
+int relattn_bf16_stream_runs(int L) { return (L + Split<STREAM_XW>::RUNQ - 1) / Split<STREAM_XW>::RUNQ; }
 
 hipError_t launch_relattn_bf16_stream(const RelAttnArgs &a, int dh, hipStream_t s)
 {
