@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
 // ---------------------------------------------------------------------------
 // dq (and the bias partial sums) from the score gradients G that dkv stored
 
-constexpr int QW = 4;               // waves per workgroup
+constexpr int QW = 8;               // waves per workgroup
 constexpr int QROWS = 16 * QW;      // queries per workgroup
 constexpr int QTHR = 64 * QW;
 constexpr int QLPT = TILE_CH / QTHR;   // 16-byte loads per thread per tile
@@ -151,11 +151,17 @@ static_assert(QLPT * QTHR == TILE_CH, "whole tiles per load round");
 static_assert(QROWS - 16 + 16 * NBT <= 64 * (RQ - 1), "a tile's bands fit in three ring quarters");
 
 // G staging: the G window of one wave and one key tile is 16 rows x GCOL
-// columns starting at an 8-aligned column; row n at 16-byte chunk GRC n.
+// columns starting at an 8-aligned column; row n at 16-byte chunk GRC n.  One
+// buffer per wave: a tile reads its whole window first, and the next tile's
+// window is loaded into the buffer after those reads have completed.
 constexpr int GCOL = 88;            // band rows 0..79 plus up to 7 columns of alignment slack
 constexpr int GRC = GCOL / 8;       // 16-byte chunks per staged row
 constexpr int GLD = (16 * GRC + 63) / 64;   // staging loads per lane
-constexpr int GBUF = GLD * 1024;    // bytes per wave and buffer
+constexpr int GBUF = GLD * 1024;    // bytes per wave
+
+// s_waitcnt immediate that waits for every LDS operation of the wave and for
+// no vector-memory or export operation
+constexpr int WAIT_LGKM_ONLY = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 
 // keep mask of one word (two bf16): element e0 and e0 + 1 kept iff their key lies in [lo, hi]
 __device__ __forceinline__ uint32_t keep2(int j, int lo, int hi)
@@ -172,11 +178,12 @@ __device__ __forceinline__ u32x2 gquad(const TXL_LDS_AS char *row, int e)
     return u32x2{__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh)};
 }
 
-__global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
+// 72 KB of LDS: two workgroups (16 waves) per CU, at most 128 registers per wave.
+__global__ __launch_bounds__(QTHR) __attribute__((amdgpu_waves_per_eu(4))) void bwd_dq_kernel(RelAttnBwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) u32x4 sk[2][TILE_CH];
     __shared__ __attribute__((aligned(16))) u32x4 sr[RQ][TILE_CH];
-    __shared__ __attribute__((aligned(16))) char sgw[2][QW][GBUF];
+    __shared__ __attribute__((aligned(16))) char sgw[QW][GBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -196,6 +203,7 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     const int kt0 = split * a.tps;
     const int kt1 = min((min(i0 + QROWS - 1, L - 1) + M) / BK + 1, kt0 + a.tps);
     const int ntile_w = i0w < L ? (min(i0w + 15, L - 1) + M) / BK + 1 : 0;
+    const int ntg = min(ntile_w, kt1);              // the wave computes tiles [kt0, ntg)
 
     // keys j with kmem <= j <= iq + M have a stored dS (dkv skips key blocks
     // that lie wholly below the valid memory)
@@ -212,16 +220,15 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
     // key tile j0; the staged window starts at the 8-aligned column below it.
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.g + (int64_t)bh * L * a.kp, (uint32_t)((int64_t)L * a.kp * 2));
     const int pcol0 = L - 16 - i0w;
-    const uint32_t sg_base = __builtin_amdgcn_readfirstlane(lds_addr(&sgw[0][wave][0]));
+    const uint32_t sg_base = __builtin_amdgcn_readfirstlane(lds_addr(&sgw[wave][0]));
     auto stage_g = [&](int kt) {
         const int cs = (pcol0 + kt * BK) & ~7;     // may be negative: those columns are masked
-        const uint32_t boff = (uint32_t)(kt & 1) * (QW * GBUF);
 #pragma unroll
         for (int e = 0; e < GLD; ++e) {
             const int q = lane + 64 * e;           // chunk q: row q / GRC, chunk q % GRC
             const int row = q / GRC, chk = q - row * GRC;
             const uint32_t goff = (uint32_t)(i0w + row) * (uint32_t)a.kp * 2 + (uint32_t)((cs + 8 * chk) * 2);
-            load_lds16(grs, goff, sg_base + boff + (uint32_t)e * 1024);
+            load_lds16(grs, goff, sg_base + (uint32_t)e * 1024);
         }
     };
 
@@ -259,12 +266,11 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqu[dt] = dqv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // the G window of a tile is staged in LDS one tile ahead (two buffers)
     if (kt0 < kt1) {
         load_k(kt0);
 #pragma unroll
         for (int q = 0; q < RQ - 1; ++q) load_r_quarter(kt0 + q);
-        if (kt0 < ntile_w) stage_g(kt0);
+        if (kt0 < ntg) stage_g(kt0);
     }
     // lane parts of LDS addresses (a 16-row block's swizzle depends on the lane only)
     int trl[NDT];
@@ -285,18 +291,33 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         const TXL_LDS_AS char *tk = lds_bytes(sk[kt & 1]);
         // this lane's staged row; element e of it is column cs + e
         const int cs = (pcol0 + j0) & ~7;
-        const TXL_LDS_AS char *grow = (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)&sgw[kt & 1][wave][0] + n * (GRC * 16);
+        const TXL_LDS_AS char *grow = (const TXL_LDS_AS char *)(const TXL_LDS_AS void *)&sgw[wave][0] + n * (GRC * 16);
         const int ec = (L - 1 - iq + j0) - cs;   // content: key j0 + k at element ec + k (>= 15 - n)
         const int ep = (pcol0 + j0) - cs;         // position: band row cc at element ep + cc (0..7)
         auto ring_blk = [&](int x0) {   // 16-row block of ring rows x0 .. x0 + 15 (x0 % 16 == 0)
             return lds_bytes(sr[(x0 >> 6) & (RQ - 1)]) + (x0 & 63) * (CPR * 16);
         };
+        // G^T operands: content (keys 32 ch + ...) and position (band rows 32 ks + ...)
+        u32x2 gcw[2][2], gpw[3][2];
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            gcw[ch][0] = gquad(grow, ec + 32 * ch + 4 * g);
+            gcw[ch][1] = gquad(grow, ec + 32 * ch + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+            gpw[ks][0] = gquad(grow, ep + 32 * ks + 4 * g);
+            gpw[ks][1] = ks < 2 ? gquad(grow, ep + 32 * ks + 16 + 4 * g) : u32x2{0u, 0u};
+        }
+        // the window has been read: load the next tile's into the buffer
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM_ONLY);
+        if (kt + 1 < ntg) stage_g(kt + 1);
         // keys outside [kmem, iq + M] have no stored dS: masked on the tiles that reach them
         const bool edge = j0 + BK - 1 > i0w + M || j0 < kmem_abs || !qok;
         // content part: dq^T += K^T . dS^T
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            u32x2 lo = gquad(grow, ec + 32 * ch + 4 * g), hi = gquad(grow, ec + 32 * ch + 16 + 4 * g);
+            u32x2 lo = gcw[ch][0], hi = gcw[ch][1];
             if (edge) {
                 const int jl = j0 + 32 * ch + 4 * g;
 #pragma unroll
@@ -313,8 +334,7 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         // k-steps (band rows 32 ks + {4 g + e, 16 + 4 g + e}; rows >= 80 are zero)
 #pragma unroll
         for (int ks = 0; ks < 3; ++ks) {
-            u32x2 lo = gquad(grow, ep + 32 * ks + 4 * g);
-            u32x2 hi = ks < 2 ? gquad(grow, ep + 32 * ks + 16 + 4 * g) : u32x2{0u, 0u};
+            u32x2 lo = gpw[ks][0], hi = gpw[ks][1];
             if (ks == 0) {
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
@@ -351,9 +371,8 @@ __global__ __launch_bounds__(QTHR) void bwd_dq_kernel(RelAttnBwdArgs a)
         if (kt + 1 < kt1) {
             load_k(kt + 1);
             load_r_quarter(kt + RQ - 1);
-            if (kt + 1 < ntile_w) stage_g(kt + 1);
         }
-        if (kt < ntile_w) tile(kt);
+        if (kt < ntg) tile(kt);
     }
 
     const float scale = a.scale;
