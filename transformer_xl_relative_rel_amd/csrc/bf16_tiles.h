@@ -31,9 +31,12 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 }
 
 // Chunk swizzle of an LDS tile of 64-element bf16 rows: chunk c of row r sits
-// at position c ^ swz(r).  Rows r and r + 1 share a pattern, so a 16-row
-// fragment read (16 lanes, one chunk each) spreads over all 8 positions.
-__device__ __forceinline__ int swz(int r) { return ((unsigned)r >> 1) & (CPR - 1); }
+// at position c ^ swz(r).  Measured with the LDS bank-conflict counter on
+// gfx950, both access patterns used on these tiles run without conflicts: a
+// 16-row fragment read (one 16-byte chunk per lane) and a transposing read
+// (8 bytes per lane from rows 4 g .. 4 g + 3); with the pattern (r >> 1) & 7
+// instead, the transposing reads take two passes.
+__device__ __forceinline__ int swz(int r) { return r & (CPR - 1); }
 
 // Orders this wave's LDS accesses for the compiler without waiting.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
@@ -113,19 +116,19 @@ __device__ __forceinline__ bf16x8 col_frag_lo(const u32x4 *tile, int rb, int dt,
 
 // The same reads with the lane part of the address computed once.  For a
 // block of rows starting at a multiple of 16, swz(row) depends on the lane
-// only: ((16 k + 4 g + (n >> 2)) >> 1) & 7 = (2 g + (n >> 3)) & 7.
+// only: (16 k + 4 g + (n >> 2)) & 7 = (4 g + (n >> 2)) & 7.
 //   row_lane_off: byte offset of lane (g, n)'s chunk (4 kk + g) in row n of
 //     the block -- row fragments;
 //   tr_lane_off: byte offset of lane (g, n)'s 8 bytes for output column
 //     block dt in rows 4 g + (n >> 2) of the block -- transposing reads.
 __device__ __forceinline__ int row_lane_off(int kk, int g, int n)
 {
-    return (n * CPR + ((4 * kk + g) ^ ((n >> 1) & (CPR - 1)))) * 16;
+    return (n * CPR + ((4 * kk + g) ^ swz(n))) * 16;
 }
 __device__ __forceinline__ int tr_lane_off(int dt, int g, int n)
 {
     const int r = 4 * g + (n >> 2);
-    return (r * CPR + ((2 * dt + ((n >> 1) & 1)) ^ ((r >> 1) & (CPR - 1)))) * 16 + 8 * (n & 1);
+    return (r * CPR + ((2 * dt + ((n >> 1) & 1)) ^ swz(r))) * 16 + 8 * (n & 1);
 }
 // Row fragment of the 16-row block at byte `blk` (row16 * CPR * 16 bytes into
 // a tile, row16 a multiple of 16) with a precomputed row_lane_off.
