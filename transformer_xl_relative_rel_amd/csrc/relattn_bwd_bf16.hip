@@ -92,50 +92,66 @@ __device__ __forceinline__ float sum16(float x)     // lanes 16k .. 16k + 15
 }
 
 // ---------------------------------------------------------------------------
-// prep: 32 rows per 256-thread workgroup, 8 threads (16 bytes each) per row.
+// prep: PREP_RPT groups of 32 rows per 256-thread workgroup, 8 threads (16 bytes
+// each) per row; a thread issues the loads of all its rows before any arithmetic.
+
+constexpr int PREP_RPT = 2;
+constexpr int PREP_ROWS = 32 * PREP_RPT;
 
 __global__ __launch_bounds__(256) void bwd_prep_kernel(RelAttnBwdArgs a)
 {
     const int t = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * 32 + (t >> 3);
     const int part = t & 7;
     const int64_t nrows = (int64_t)a.B * a.H * a.L;
-    const bool ok = row < nrows;
-    const int64_t rr = ok ? row : 0;
-    const int bh = (int)(rr / a.L), i = (int)(rr - (int64_t)bh * a.L);
-    const int b = bh / a.H, h = bh - b * a.H;
-    float dsum = 0.f, lse = 0.f;
-    if (ok) {
+    int64_t rr[PREP_RPT];
+    bool ok[PREP_RPT];
+    u32x4 raw[PREP_RPT], o[PREP_RPT], d[PREP_RPT];
+    f32x4 u0[PREP_RPT], u1[PREP_RPT], w0[PREP_RPT], w1[PREP_RPT];
+    float lse[PREP_RPT];
+#pragma unroll
+    for (int k = 0; k < PREP_RPT; ++k) {
+        const int64_t row = (int64_t)blockIdx.x * PREP_ROWS + 32 * k + (t >> 3);
+        ok[k] = row < nrows;
+        rr[k] = ok[k] ? row : 0;
+        const int bh = (int)(rr[k] / a.L), i = (int)(rr[k] - (int64_t)bh * a.L);
+        const int b = bh / a.H, h = bh - b * a.H;
         // every load first, so that a thread waits for one memory round trip
         // (stores to qu and qv may alias out or dout as far as the compiler
-        // knows, so it would not move those loads above them)
+        // knows, so it would not move those loads above them); rows past the
+        // end read row 0 and store nothing
         const uint16_t *qp = static_cast<const uint16_t *>(a.q) + b * a.qs[0] + h * a.qs[1] + (int64_t)i * a.qs[2];
         const int64_t ooff = b * a.os[0] + h * a.os[1] + (int64_t)i * a.os[2] + 8 * part;
-        const u32x4 raw = *reinterpret_cast<const u32x4 *>(qp + 8 * part);
-        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.out) + ooff);
-        const u32x4 d = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.dout) + ooff);
+        raw[k] = *reinterpret_cast<const u32x4 *>(qp + 8 * part);
+        o[k] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.out) + ooff);
+        d[k] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.dout) + ooff);
         const f32x4 *up = reinterpret_cast<const f32x4 *>(a.u + h * DH + 8 * part);
         const f32x4 *wp = reinterpret_cast<const f32x4 *>(a.vb + h * DH + 8 * part);
-        const f32x4 u0 = up[0], u1 = up[1], w0 = wp[0], w1 = wp[1];
-        lse = a.lse[rr];
-        __builtin_amdgcn_sched_barrier(0);   // no arithmetic (and so no wait) between the loads
+        u0[k] = up[0]; u1[k] = up[1]; w0[k] = wp[0]; w1[k] = wp[1];
+        lse[k] = a.lse[rr[k]];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // no arithmetic (and so no wait) between the loads
+#pragma unroll
+    for (int k = 0; k < PREP_RPT; ++k) {
         f32x8 fu, fv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = bf16_val((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-            fu[e] = (x + (e < 4 ? u0[e & 3] : u1[e & 3])) * a.c;     // same operation order as the forward's query operands
-            fv[e] = (x + (e < 4 ? w0[e & 3] : w1[e & 3])) * a.c;
+            const float x = bf16_val((raw[k][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            fu[e] = (x + (e < 4 ? u0[k][e & 3] : u1[k][e & 3])) * a.c;     // same operation order as the forward's query operands
+            fv[e] = (x + (e < 4 ? w0[k][e & 3] : w1[k][e & 3])) * a.c;
         }
+        float dsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            dsum += bf16_val((o[e >> 1] >> (16 * (e & 1))) & 0xffffu) * bf16_val((d[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        *reinterpret_cast<bf16x8 *>(a.qu + rr * DH + 8 * part) = __builtin_convertvector(fu, bf16x8);
-        *reinterpret_cast<bf16x8 *>(a.qv + rr * DH + 8 * part) = __builtin_convertvector(fv, bf16x8);
-    }
-    dsum = sum8(dsum);
-    if (ok && part == 0) {
-        a.dd[rr] = dsum;
-        a.lse2[rr] = lse * LOG2E;
+            dsum += bf16_val((o[k][e >> 1] >> (16 * (e & 1))) & 0xffffu) * bf16_val((d[k][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        if (ok[k]) {
+            *reinterpret_cast<bf16x8 *>(a.qu + rr[k] * DH + 8 * part) = __builtin_convertvector(fu, bf16x8);
+            *reinterpret_cast<bf16x8 *>(a.qv + rr[k] * DH + 8 * part) = __builtin_convertvector(fv, bf16x8);
+        }
+        dsum = sum8(dsum);
+        if (ok[k] && part == 0) {
+            a.dd[rr[k]] = dsum;
+            a.lse2[rr[k]] = lse[k] * LOG2E;
+        }
     }
 }
 
@@ -950,7 +966,7 @@ hipError_t launch_relattn_bwd_bf16(const RelAttnBwdArgs &a, hipStream_t s)
 {
     const int64_t rows = (int64_t)a.B * a.H * a.L;
     const int BH = a.B * a.H;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + PREP_ROWS - 1) / PREP_ROWS)), dim3(256), 0, s, a);
     // dkv stores the score gradients G that dq and dr read
     hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(BH * ((a.K + KBLK - 1) / KBLK))), dim3(KTHR), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * ((a.L + QROWS - 1) / QROWS) * a.nsplit)), dim3(QTHR), 0, s, a);
