@@ -30,10 +30,11 @@
 //          pass from the score MFMA's result layout to the operand layout
 //          without data movement).  It also stores dS of the visible pairs as
 //          G[i][L-1-i+j] (bf16) to the workspace.
-//   dq   : one wave per 16 queries, 4 waves per workgroup, keys in tiles of
+//   dq   : one wave per 16 queries, 8 waves per workgroup, keys in tiles of
 //          64, transposed (head columns on MFMA rows, queries on lanes).  The
 //          wave's G window of a tile (16 rows x 88 columns) is staged in LDS
-//          with direct loads; dq^T += K^T . dS^T reads dS at key positions
+//          with direct loads into one buffer per wave, refilled for the next
+//          tile once the wave has read it; dq^T += K^T . dS^T reads dS at key positions
 //          (row i shifted by L-1-i: aligned words and a byte shift), and
 //          dq^T += R_band^T . G^T reads the same rows at band positions.  Per
 //          16-query sums of both parts go to the workspace for du and dvb.
